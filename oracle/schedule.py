@@ -1,0 +1,311 @@
+"""Instruction tensor: an independent builder, a validator and a simulator.
+
+The persistent-kernel idea this serves: one kernel occupies the whole GPU and
+each block reads a host-built instruction tensor to decide its next work
+(Kittens VM summary, "Method"); the blocks get "a schedule of every operation
+in the forward pass" and synchronise on the device (Hyperkernel teardown,
+"What a megakernel buys").  The pages fix no format, tiling or assignment, so
+the tensor below is this project's own specification ("schedule spec v1",
+written out in the design notes); the GPU library's C++ builder must produce
+the same bytes.
+
+Spec v1 (all int32):
+
+* stage order per token: for each layer ``QKV, ATTN, [AREDUCE if n_chunks > 1],
+  OPROJ, UPGATE|MOE_UPGATE, DOWN|MOE_DOWN``; then ``LMHEAD``.
+* a GEMV stage over R rows has ``n = min(n_wg, R)`` tiles; tile i covers rows
+  ``[i*R//n, (i+1)*R//n)``.  R: QKV = qd + 2 kvd, OPROJ = DOWN = MOE_DOWN = d,
+  UPGATE = F, MOE_UPGATE = top_k * F, LMHEAD = V.
+* ATTN has ``hkv * n_chunks`` instructions (kv_head = i // n_chunks,
+  chunk = i % n_chunks); AREDUCE has hq (q_head = i).
+* instruction i of a stage goes to block ``i % n_wg``; a block's list is the
+  concatenation of its instructions in stage order.
+* words: header[16] = {magic, version, n_wg, n_stages, max_instr, n_chunks, L,
+  d, hq, hkv, hd, F, V, E, top_k, total_instr}; counts[n_wg]; then
+  ``[n_wg][max_instr][16]`` with instruction = {opcode, layer, stage, index,
+  a, b, wait_stage, wait_count, wait_prev_token, signal_stage, 0...};
+  ``a, b`` = row range (GEMV), (kv_head, chunk) (ATTN), (q_head, 0)
+  (AREDUCE); ``wait_stage`` is the stage whose outputs the instruction reads
+  (QKV of layer 0 reads the previous token's LMHEAD: wait_prev_token = 1);
+  LMHEAD's layer field is L.  Unused slots are zero.
+
+Parity pins: tests check the validator invariants (every row of every stage
+produced exactly once, waits name the producing stage and its size, lists in
+stage order) and the simulator (no deadlock and no overwrite of a value that
+a pending instruction still needs, over random interleavings).
+"""
+from __future__ import annotations
+
+import random
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+MAGIC = 0x314B444D
+VERSION = 1
+WORDS = 16
+
+OP_QKV, OP_ATTN, OP_AREDUCE, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD = range(1, 10)
+OP_NAMES = {OP_QKV: "QKV", OP_ATTN: "ATTN", OP_AREDUCE: "AREDUCE", OP_OPROJ: "OPROJ",
+            OP_UPGATE: "UPGATE", OP_DOWN: "DOWN", OP_MOE_UPGATE: "MOE_UPGATE",
+            OP_MOE_DOWN: "MOE_DOWN", OP_LMHEAD: "LMHEAD"}
+GEMV_OPS = (OP_QKV, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD)
+
+
+def stages(cfg, n_chunks: int) -> List[Tuple[int, int, int]]:
+    """(opcode, layer, rows-or-count) for every stage of one token, in order."""
+    out = []
+    qkv_rows = cfg.qd + 2 * cfg.kvd
+    for l in range(cfg.n_layers):
+        out.append((OP_QKV, l, qkv_rows))
+        out.append((OP_ATTN, l, cfg.n_kv_heads * n_chunks))
+        if n_chunks > 1:
+            out.append((OP_AREDUCE, l, cfg.n_q_heads))
+        out.append((OP_OPROJ, l, cfg.d_model))
+        if cfg.is_moe:
+            out.append((OP_MOE_UPGATE, l, cfg.top_k * cfg.d_ff))
+            out.append((OP_MOE_DOWN, l, cfg.d_model))
+        else:
+            out.append((OP_UPGATE, l, cfg.d_ff))
+            out.append((OP_DOWN, l, cfg.d_model))
+    out.append((OP_LMHEAD, cfg.n_layers, cfg.vocab))
+    return out
+
+
+def stage_instructions(op: int, layer: int, size: int, n_wg: int, n_chunks: int) -> List[Tuple[int, int]]:
+    """The (a, b) operand pairs of one stage's instructions, by index."""
+    if op in GEMV_OPS:
+        n = min(n_wg, size)
+        return [(i * size // n, (i + 1) * size // n) for i in range(n)]
+    if op == OP_ATTN:
+        return [(i // n_chunks, i % n_chunks) for i in range(size)]
+    if op == OP_AREDUCE:
+        return [(i, 0) for i in range(size)]
+    raise ValueError(op)
+
+
+def build(cfg, n_wg: int, n_chunks: int) -> np.ndarray:
+    """Instruction tensor (int32 words) for ``cfg`` on ``n_wg`` blocks."""
+    if n_wg < 1 or n_chunks < 1:
+        raise ValueError("n_wg and n_chunks must be >= 1")
+    st = stages(cfg, n_chunks)
+    n_st = len(st)
+    lists: List[List[List[int]]] = [[] for _ in range(n_wg)]
+    counts_per_stage = [len(stage_instructions(op, l, sz, n_wg, n_chunks)) for op, l, sz in st]
+    for s, (op, l, sz) in enumerate(st):
+        if s == 0:
+            wait_stage, wait_prev = n_st - 1, 1
+        else:
+            wait_stage, wait_prev = s - 1, 0
+        for i, (a, b) in enumerate(stage_instructions(op, l, sz, n_wg, n_chunks)):
+            words = [op, l, s, i, a, b, wait_stage, counts_per_stage[wait_stage], wait_prev, s]
+            words += [0] * (WORDS - len(words))
+            lists[i % n_wg].append(words)
+    max_instr = max(len(x) for x in lists)
+    total = sum(len(x) for x in lists)
+    hdr = [MAGIC, VERSION, n_wg, n_st, max_instr, n_chunks, cfg.n_layers, cfg.d_model,
+           cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ff, cfg.vocab,
+           cfg.n_experts, cfg.top_k, total]
+    body = np.zeros((n_wg, max_instr, WORDS), dtype=np.int32)
+    for w, lst in enumerate(lists):
+        if lst:
+            body[w, :len(lst)] = np.asarray(lst, dtype=np.int32)
+    counts = np.array([len(x) for x in lists], dtype=np.int32)
+    return np.concatenate([np.asarray(hdr, dtype=np.int32), counts, body.reshape(-1)])
+
+
+def parse(words: np.ndarray) -> Tuple[List[int], List[List[List[int]]]]:
+    words = np.asarray(words, dtype=np.int32)
+    hdr = [int(x) for x in words[:WORDS]]
+    n_wg, max_instr = hdr[2], hdr[4]
+    counts = [int(x) for x in words[WORDS:WORDS + n_wg]]
+    body = words[WORDS + n_wg:].reshape(n_wg, max_instr, WORDS)
+    lists = [[[int(v) for v in body[w, j]] for j in range(counts[w])] for w in range(n_wg)]
+    return hdr, lists
+
+
+def validate(words: np.ndarray, cfg) -> None:
+    """Raise ValueError unless the tensor satisfies the spec's invariants."""
+    hdr, lists = parse(words)
+    if hdr[0] != MAGIC or hdr[1] != VERSION:
+        raise ValueError("bad magic/version")
+    n_wg, n_st, max_instr, n_chunks = hdr[2], hdr[3], hdr[4], hdr[5]
+    st = stages(cfg, n_chunks)
+    if n_st != len(st):
+        raise ValueError("stage count")
+    seen: Dict[int, List[Tuple[int, int]]] = {s: [] for s in range(n_st)}
+    for w, lst in enumerate(lists):
+        prev = -1
+        for ins in lst:
+            op, l, s, i, a, b, ws, wc, wp, sig = ins[:10]
+            if not (0 <= s < n_st) or st[s][0] != op or st[s][1] != l:
+                raise ValueError(f"wg {w}: stage/opcode mismatch {ins}")
+            if s < prev:
+                raise ValueError(f"wg {w}: list not in stage order")
+            prev = s
+            if i % n_wg != w:
+                raise ValueError(f"wg {w}: instruction {i} of stage {s} on the wrong block")
+            if sig != s:
+                raise ValueError("signal stage")
+            want_ws = n_st - 1 if s == 0 else s - 1
+            if ws != want_ws or wp != (1 if s == 0 else 0):
+                raise ValueError("wait stage")
+            seen[s].append((i, a, b))
+    for s, (op, l, sz) in enumerate(st):
+        got = sorted(seen[s])
+        want = stage_instructions(op, l, sz, n_wg, n_chunks)
+        if [x[0] for x in got] != list(range(len(want))):
+            raise ValueError(f"stage {s}: instruction indices")
+        if [(x[1], x[2]) for x in got] != want:
+            raise ValueError(f"stage {s}: operands")
+        if op in GEMV_OPS:
+            rows = np.zeros(sz, dtype=np.int64)
+            for _, a, b in got:
+                rows[a:b] += 1
+            if not np.all(rows == 1):
+                raise ValueError(f"stage {s}: rows not covered exactly once")
+    for s, (op, l, sz) in enumerate(st):
+        n_prod = len(seen[n_st - 1 if s == 0 else s - 1])
+        for w, lst in enumerate(lists):
+            for ins in lst:
+                if ins[2] == s and ins[7] != n_prod:
+                    raise ValueError("wait count")
+
+
+# ----------------------------------------------------------------------------
+# simulator: what each instruction reads and writes, and a random interleaver
+# ----------------------------------------------------------------------------
+
+def chunk_range(T: int, n_chunks: int, c: int) -> Tuple[int, int]:
+    """Positions [lo, hi) of split-KV chunk c when T positions are visible:
+    chunk length = ceil(T / n_chunks) rounded up to a multiple of 16."""
+    clen = ((T + n_chunks - 1) // n_chunks + 15) // 16 * 16
+    return min(T, c * clen), min(T, (c + 1) * clen)
+
+
+def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_lm_tiles: int, t: int, start_pos: int):
+    """Element reads and writes of one instruction at token t.
+
+    Buffers hold tagged values; a read of (buffer, element) expects the
+    version written at ``(t, layer)`` named in the tuple.  Buffers: 'h'
+    (residual entering a layer), 'qkv', 'part' (attention partials),
+    'aout', 'hmid', 'act', 'route', 'lm' (per-tile max/argmax), and 'kv'
+    (cache rows, element = (layer, kv_head, position); version = token that
+    appended it, -1 for the context present before the run).
+    """
+    op, l, s, i, a, b = ins[:6]
+    d, qd, kvd, hd, G = cfg.d_model, cfg.qd, cfg.kvd, cfg.head_dim, cfg.group
+    reads: List[Tuple[str, int, Tuple[int, int]]] = []
+    writes: List[Tuple[str, int, Tuple[int, int]]] = []
+
+    def token_reads():
+        if t > 0:
+            for k in range(n_lm_tiles):
+                reads.append(("lm", k, (t - 1, cfg.n_layers)))
+
+    if op == OP_QKV:
+        if l == 0:
+            token_reads()
+        else:
+            reads.extend(("h", r, (t, l)) for r in range(d))
+        writes.extend(("qkv", r, (t, l)) for r in range(a, b))
+    elif op == OP_ATTN:
+        kvh, c = a, b
+        pos = start_pos + t
+        lo, hi = chunk_range(pos + 1, n_chunks, c)
+        for j in range(lo, hi):
+            if j < pos:
+                reads.append(("kv", (l, kvh, j), (j - start_pos if j >= start_pos else -1, 0)))
+        if lo <= pos < hi:
+            writes.append(("kv", (l, kvh, pos), (t, 0)))
+        rows = list(range(kvh * G * hd, (kvh + 1) * G * hd))
+        rows += list(range(qd + kvh * hd, qd + (kvh + 1) * hd))
+        rows += list(range(qd + kvd + kvh * hd, qd + kvd + (kvh + 1) * hd))
+        reads.extend(("qkv", r, (t, l)) for r in rows)
+        if n_chunks > 1:
+            for j in range(kvh * G, (kvh + 1) * G):
+                writes.append(("part", j * n_chunks + c, (t, l)))
+        else:
+            writes.extend(("aout", r, (t, l)) for r in range(kvh * G * hd, (kvh + 1) * G * hd))
+    elif op == OP_AREDUCE:
+        j = a
+        reads.extend(("part", j * n_chunks + c, (t, l)) for c in range(n_chunks))
+        writes.extend(("aout", r, (t, l)) for r in range(j * hd, (j + 1) * hd))
+    elif op == OP_OPROJ:
+        reads.extend(("aout", r, (t, l)) for r in range(qd))
+        if l == 0:
+            token_reads()
+        else:
+            reads.extend(("h", r, (t, l)) for r in range(a, b))
+        writes.extend(("hmid", r, (t, l)) for r in range(a, b))
+    elif op in (OP_UPGATE, OP_MOE_UPGATE):
+        reads.extend(("hmid", r, (t, l)) for r in range(d))
+        writes.extend(("act", r, (t, l)) for r in range(a, b))
+        if op == OP_MOE_UPGATE and i == 0:
+            writes.append(("route", 0, (t, l)))
+    elif op in (OP_DOWN, OP_MOE_DOWN):
+        n_act = cfg.d_ff * (cfg.top_k if op == OP_MOE_DOWN else 1)
+        reads.extend(("act", r, (t, l)) for r in range(n_act))
+        if op == OP_MOE_DOWN:
+            reads.append(("route", 0, (t, l)))
+        reads.extend(("hmid", r, (t, l)) for r in range(a, b))
+        writes.extend(("h", r, (t, l + 1)) for r in range(a, b))
+    elif op == OP_LMHEAD:
+        reads.extend(("h", r, (t, l)) for r in range(d))
+        writes.append(("lm", i, (t, l)))
+    return reads, writes
+
+
+def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos: int = 0) -> None:
+    """Run every block's list under a random interleaving of tagged buffers.
+
+    An instruction may run when every element it reads holds the version it
+    expects.  Raises on deadlock (no block can run) and on a write that would
+    replace a version some pending instruction still has to read.
+    """
+    hdr, lists = parse(words)
+    n_wg, n_chunks = hdr[2], hdr[5]
+    n_lm = min(n_wg, cfg.vocab)
+    rng = random.Random(seed)
+    mem: Dict[Tuple[str, object], Tuple[int, int]] = {}
+    for l in range(cfg.n_layers):
+        for h in range(cfg.n_kv_heads):
+            for j in range(start_pos):
+                mem[("kv", (l, h, j))] = (-1, 0)
+    # every (token, block, position) as a job in program order
+    progs = [[(t, ins) for t in range(n_tokens) for ins in lst] for lst in lists]
+    pc = [0] * n_wg
+    # pending reads per (buffer, element, version): how many unfinished
+    # instructions still need that version
+    need: Dict[Tuple[str, int, Tuple[int, int]], int] = {}
+    sets = []
+    for w in range(n_wg):
+        sw = []
+        for t, ins in progs[w]:
+            r, wr = _rw_sets(cfg, ins, n_chunks, n_lm, t, start_pos)
+            sw.append((r, wr))
+            for (buf, e, v) in r:
+                need[(buf, e, v)] = need.get((buf, e, v), 0) + 1
+        sets.append(sw)
+    remaining = sum(len(p) for p in progs)
+    while remaining:
+        runnable = []
+        for w in range(n_wg):
+            if pc[w] < len(progs[w]):
+                r, _ = sets[w][pc[w]]
+                if all(mem.get((buf, e)) == v for (buf, e, v) in r):
+                    runnable.append(w)
+        if not runnable:
+            stuck = [(w, progs[w][pc[w]][1][:6]) for w in range(n_wg) if pc[w] < len(progs[w])]
+            raise RuntimeError(f"deadlock: {stuck[:4]}")
+        w = rng.choice(runnable)
+        r, wr = sets[w][pc[w]]
+        for (buf, e, v) in r:
+            need[(buf, e, v)] -= 1
+        for (buf, e, v) in wr:
+            old = mem.get((buf, e))
+            if old is not None and need.get((buf, e, old), 0) > 0:
+                raise RuntimeError(f"overwrite hazard: {buf}[{e}] {old} -> {v} by wg {w}")
+            mem[(buf, e)] = v
+        pc[w] += 1
+        remaining -= 1
