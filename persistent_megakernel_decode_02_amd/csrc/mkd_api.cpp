@@ -1,0 +1,483 @@
+// Host side of the C ABI declared in include/mkd.h.
+//
+// The host records pointers, computes the RoPE table, builds and uploads the
+// instruction tensor and launches; it never needs to understand the model
+// beyond shapes (Hyperkernel teardown, "What is in the repository": the host
+// copies tensors to the addresses the plan names and launches).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <chrono>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "mkd_internal.h"
+
+using namespace mkd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MKD_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+}  // namespace
+
+struct mkd_model {
+  mkd_config cfg{};
+  int device = 0;
+  int n_cu = 0;
+  int32_t max_seq = 0;
+  uint16_t* kv = nullptr;
+  std::vector<uint64_t> wptr;
+  uint64_t* d_wtab = nullptr;
+  float* d_rope = nullptr;
+  int32_t* d_status = nullptr;
+  int32_t* h_stop = nullptr;
+  uint64_t* d_ll = nullptr;
+  size_t ll_words = 0, ll_cap = 0;
+  // sub-buffers of d_ll
+  uint64_t *h = nullptr, *qkv = nullptr, *part = nullptr, *aout = nullptr, *hmid = nullptr,
+           *act = nullptr, *route = nullptr, *lm = nullptr;
+  int32_t* d_sched = nullptr;
+  size_t sched_words = 0, sched_cap = 0;
+  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0;
+  hipEvent_t done = nullptr;
+  bool launched = false;
+  double clock_hz = 100e6;
+  uint64_t watchdog_ticks = 0;
+  uint64_t* trace = nullptr;
+  size_t trace_cap = 0;
+};
+
+extern "C" {
+
+int mkd_version(void) { return MKD_ABI_VERSION; }
+
+const char* mkd_last_error(void) { return g_err.c_str(); }
+
+int mkd_config_check(const mkd_config* cfg) {
+  const char* why = "";
+  const int rc = config_check(cfg, &why);
+  if (rc) return fail(rc, why);
+  return MKD_OK;
+}
+
+int mkd_weight_count(const mkd_config* cfg, size_t* n_out) {
+  int rc = mkd_config_check(cfg);
+  if (rc) return rc;
+  if (!n_out) return fail(MKD_E_INVALID, "null n_out");
+  *n_out = (size_t)(cfg->tied ? 2 : 3) + (size_t)cfg->n_layers * layer_slots(cfg);
+  return MKD_OK;
+}
+
+int mkd_weight_shape(const mkd_config* cfg, size_t index, int64_t* rows, int64_t* cols) {
+  size_t n = 0;
+  int rc = mkd_weight_count(cfg, &n);
+  if (rc) return rc;
+  if (index >= n || !rows || !cols) return fail(MKD_E_INVALID, "weight index out of range");
+  const int64_t d = cfg->d_model, F = cfg->d_ff, V = cfg->vocab;
+  const int64_t qd = (int64_t)cfg->n_q_heads * cfg->head_dim, kvd = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  const size_t g = cfg->tied ? 2 : 3;
+  if (index < g) {
+    if (index == 1) { *rows = d; *cols = 1; }
+    else { *rows = V; *cols = d; }  // embed, lm_head
+    return MKD_OK;
+  }
+  const int k = (int)((index - g) % layer_slots(cfg));
+  switch (k) {
+    case WL_ATTN_NORM: case WL_FFN_NORM: *rows = d; *cols = 1; return MKD_OK;
+    case WL_Q: *rows = qd; *cols = d; return MKD_OK;
+    case WL_K: case WL_V: *rows = kvd; *cols = d; return MKD_OK;
+    case WL_O: *rows = d; *cols = qd; return MKD_OK;
+    default: break;
+  }
+  if (!cfg->n_experts) {
+    if (k == WL_DOWN) { *rows = d; *cols = F; }
+    else { *rows = F; *cols = d; }
+    return MKD_OK;
+  }
+  if (k == WL_ROUTER) { *rows = cfg->n_experts; *cols = d; return MKD_OK; }
+  const int e = k - WL_EXPERTS;  // gate[E], up[E], down[E]
+  if (e < 2 * cfg->n_experts) { *rows = F; *cols = d; }
+  else { *rows = d; *cols = F; }
+  return MKD_OK;
+}
+
+int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out) {
+  int rc = mkd_config_check(cfg);
+  if (rc) return rc;
+  if (max_seq < 1 || !bytes_out) return fail(MKD_E_INVALID, "max_seq must be >= 1");
+  *bytes_out = (size_t)cfg->n_layers * 2 * cfg->n_kv_heads * (size_t)max_seq * cfg->head_dim * 2;
+  return MKD_OK;
+}
+
+int mkd_schedule_build(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t* out,
+                       size_t capacity, size_t* n_words) {
+  const char* why = "";
+  const int rc = schedule_build(cfg, n_wg, n_chunks, out, capacity, n_words, &why);
+  if (rc) return fail(rc, why);
+  return MKD_OK;
+}
+
+int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_words) {
+  const char* why = "";
+  const int rc = schedule_validate(cfg, words, n_words, &why);
+  if (rc) return fail(rc, why);
+  return MKD_OK;
+}
+
+int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
+             int32_t max_seq, int32_t device, mkd_model** out) {
+  if (!out) return fail(MKD_E_INVALID, "null out");
+  *out = nullptr;
+  size_t want = 0;
+  int rc = mkd_weight_count(cfg, &want);
+  if (rc) return rc;
+  if (!weights || n_weights != want)
+    return fail(MKD_E_INVALID, "expected " + std::to_string(want) + " weight pointers, got " +
+                                   std::to_string(n_weights));
+  for (size_t i = 0; i < n_weights; ++i) {
+    if (!weights[i] || ((uintptr_t)weights[i] & 15))
+      return fail(MKD_E_INVALID, "weight " + std::to_string(i) + " is null or not 16-byte aligned");
+  }
+  if (max_seq < 1) return fail(MKD_E_INVALID, "max_seq must be >= 1");
+  if (!kv_cache || ((uintptr_t)kv_cache & 15)) return fail(MKD_E_INVALID, "kv_cache null or misaligned");
+  const size_t head_bytes = (size_t)max_seq * cfg->head_dim * 2;
+  if (head_bytes > 0x7fffffffull) return fail(MKD_E_INVALID, "max_seq * head_dim too large");
+
+  hipError_t e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MKD_E_UNSUPPORTED, std::string("library is built for gfx950, device is ") + prop.gcnArchName);
+  int coop = 0;
+  hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device);
+  if (!coop) return fail(MKD_E_UNSUPPORTED, "device lacks cooperative launch");
+
+  mkd_model* m = new mkd_model();
+  m->cfg = *cfg;
+  m->device = device;
+  m->n_cu = prop.multiProcessorCount;
+  m->max_seq = max_seq;
+  m->kv = (uint16_t*)kv_cache;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+    m->clock_hz = (double)khz * 1e3;
+  m->watchdog_ticks = (uint64_t)(2.0 * m->clock_hz);
+
+  // pointer table: embed, final_norm, lm_head (embed when tied), then layers
+  const int ls = layer_slots(cfg);
+  m->wptr.assign(W_GLOBAL + (size_t)cfg->n_layers * ls, 0);
+  size_t k = 0;
+  m->wptr[W_EMBED] = (uint64_t)weights[k++];
+  m->wptr[W_FINAL_NORM] = (uint64_t)weights[k++];
+  m->wptr[W_LM_HEAD] = cfg->tied ? m->wptr[W_EMBED] : (uint64_t)weights[k++];
+  for (int l = 0; l < cfg->n_layers; ++l)
+    for (int s = 0; s < ls; ++s) m->wptr[W_GLOBAL + (size_t)l * ls + s] = (uint64_t)weights[k++];
+
+  // RoPE table: angle = pos * theta^(-2i/hd) in fp64, cos and sin rounded to fp32
+  const int half = cfg->head_dim / 2;
+  std::vector<float> rope((size_t)2 * max_seq * half);
+  for (int pos = 0; pos < max_seq; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)pos * pow(cfg->rope_theta, (-2.0 * i) / cfg->head_dim);
+      rope[(size_t)pos * half + i] = (float)cos(a);
+      rope[(size_t)max_seq * half + (size_t)pos * half + i] = (float)sin(a);
+    }
+
+  auto cleanup = [&](int code, const std::string& msg) {
+    mkd_destroy(m);
+    return fail(code, msg);
+  };
+  if ((e = hipMalloc(&m->d_wtab, m->wptr.size() * 8)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc wtab");
+  if ((e = hipMalloc(&m->d_rope, rope.size() * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc rope");
+  if ((e = hipMalloc(&m->d_status, S_WORDS * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc status");
+  if ((e = hipHostMalloc(&m->h_stop, 64, hipHostMallocDefault)) != hipSuccess)
+    return cleanup(MKD_E_HIP, "hipHostMalloc stop word");
+  memset(m->h_stop, 0, 64);
+  if ((e = hipMemcpy(m->d_wtab, m->wptr.data(), m->wptr.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
+    return cleanup(MKD_E_HIP, "upload wtab");
+  if ((e = hipMemcpy(m->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return cleanup(MKD_E_HIP, "upload rope");
+  if ((e = hipMemset(m->d_status, 0, S_WORDS * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "clear status");
+  if ((e = hipEventCreateWithFlags(&m->done, hipEventDisableTiming)) != hipSuccess)
+    return cleanup(MKD_E_HIP, "hipEventCreate");
+  *out = m;
+  return MKD_OK;
+}
+
+// LDS floats for the GEMV row results of the largest tile (x2 for the
+// opcodes that stream two rows per output row)
+static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
+  const int n_st = stage_count(c, n_chunks);
+  std::vector<StageDesc> st(n_st);
+  int got = 0;
+  stage_list(c, n_chunks, st.data(), &got, n_st);
+  int best = 4;
+  for (const StageDesc& s : st) {
+    if (!is_gemv(s.op)) continue;
+    const int n = s.size < n_wg ? s.size : n_wg;
+    int rows = (s.size + n - 1) / n;
+    if (s.op == OP_UPGATE || s.op == OP_MOE_UPGATE || s.op == OP_MOE_DOWN) rows *= 2;
+    best = rows > best ? rows : best;
+  }
+  return (best + 3) & ~3;
+}
+
+static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm) {
+  const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
+  const int qd = c->n_q_heads * hd;
+  int x = c->d_model;
+  x = x > qd ? x : qd;
+  const int act = c->d_ff * (c->top_k ? c->top_k : 1);
+  x = x > act ? x : act;
+  x = x > 2 * n_lm ? x : 2 * n_lm;
+  const int ared = n_chunks * (hd + 2);
+  x = x > ared ? x : ared;
+  const int attn = (G + 2) * hd + kWaves * G * (hd + 2);
+  x = x > attn ? x : attn;
+  return (x + 3) & ~3;
+}
+
+int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (n_cu) *n_cu = m->n_cu;
+  if (max_coop_wg) {
+    KParams p{};
+    p.x_floats = x_floats_for(&m->cfg, 1, m->n_cu);
+    p.out_floats = out_floats_for(&m->cfg, m->n_cu, 1);
+    p.d = m->cfg.d_model;
+    int mx = 0;
+    const int rc = max_coop_blocks(m->device, lds_bytes(p), &mx);
+    if (rc) return fail(rc, "occupancy query failed");
+    *max_coop_wg = mx;
+  }
+  return MKD_OK;
+}
+
+static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
+  const mkd_config* c = &m->cfg;
+  const int n_wg = words[H_NWG], n_chunks = words[H_NCHUNKS];
+  if (n_chunks > 64) return fail(MKD_E_UNSUPPORTED, "n_chunks > 64 is not supported by the device code");
+  if (n_wg > 4096) return fail(MKD_E_UNSUPPORTED, "n_wg > 4096 is not supported by the device code");
+  const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
+  const int x_floats = x_floats_for(c, n_chunks, n_lm);
+  const int out_floats = out_floats_for(c, n_wg, n_chunks);
+  KParams p{};
+  p.x_floats = x_floats;
+  p.out_floats = out_floats;
+  p.d = c->d_model;
+  const size_t lds = lds_bytes(p);
+  int lds_max = 0;
+  hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
+  if (lds_max > 0 && lds > (size_t)lds_max)
+    return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
+                                       std::to_string(lds_max) + " (use more workgroups)");
+  int mx = 0;
+  int rc = max_coop_blocks(m->device, lds, &mx);
+  if (rc) return fail(rc, "occupancy query failed");
+  if (n_wg > mx)
+    return fail(MKD_E_COOPERATIVE, "n_wg " + std::to_string(n_wg) + " exceeds the " +
+                                       std::to_string(mx) + " workgroups that can be co-resident");
+  hipError_t e = hipSetDevice(m->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  if (m->launched) hipEventSynchronize(m->done);
+  if (n > m->sched_cap) {
+    if (m->d_sched) hipFree(m->d_sched);
+    m->d_sched = nullptr;
+    m->sched_cap = 0;
+    if ((e = hipMalloc(&m->d_sched, n * 4)) != hipSuccess) return hip_fail(e, "hipMalloc schedule");
+    m->sched_cap = n;
+  }
+  if ((e = hipMemcpy(m->d_sched, words, n * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(e, "upload schedule");
+  m->sched_words = n;
+  // tagged activation buffers, one allocation (cleared before each launch)
+  const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  const size_t sz[8] = {round16(c->d_model), round16(qd + 2 * kvd),
+                        round16((size_t)c->n_q_heads * n_chunks * (c->head_dim + 2)), round16(qd),
+                        round16(c->d_model), round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1)),
+                        16, round16(2 * (size_t)n_lm)};
+  size_t total = 0;
+  for (size_t s : sz) total += s;
+  if (total > m->ll_cap) {
+    if (m->d_ll) hipFree(m->d_ll);
+    m->d_ll = nullptr;
+    m->ll_cap = 0;
+    if ((e = hipMalloc(&m->d_ll, total * 8)) != hipSuccess) return hip_fail(e, "hipMalloc activations");
+    m->ll_cap = total;
+  }
+  m->ll_words = total;
+  uint64_t* q = m->d_ll;
+  uint64_t** dst[8] = {&m->h, &m->qkv, &m->part, &m->aout, &m->hmid, &m->act, &m->route, &m->lm};
+  for (int i = 0; i < 8; ++i) { *dst[i] = q; q += sz[i]; }
+  m->n_wg = n_wg;
+  m->n_chunks = n_chunks;
+  m->max_instr = words[H_MAXINSTR];
+  m->n_lm = n_lm;
+  m->x_floats = x_floats;
+  m->out_floats = out_floats;
+  return MKD_OK;
+}
+
+int mkd_load_schedule(mkd_model* m, const int32_t* words, size_t n_words) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  int rc = mkd_schedule_validate(&m->cfg, words, n_words);
+  if (rc) return rc;
+  return upload_schedule(m, words, n_words);
+}
+
+int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks, int32_t* host_out,
+                       size_t capacity, size_t* n_words) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (n_wg == 0) n_wg = m->n_cu;
+  if (n_chunks == 0) {
+    const double head_bytes = (double)m->max_seq * m->cfg.head_dim * 4.0;  // K and V rows
+    int want = (int)ceil(head_bytes / 32768.0);
+    int cap = n_wg / m->cfg.n_kv_heads;
+    cap = cap < 1 ? 1 : (cap > 64 ? 64 : cap);
+    n_chunks = want < 1 ? 1 : (want > cap ? cap : want);
+  }
+  size_t n = 0;
+  int rc = mkd_schedule_build(&m->cfg, n_wg, n_chunks, nullptr, 0, &n);
+  if (rc) return rc;
+  std::vector<int32_t> w(n);
+  rc = mkd_schedule_build(&m->cfg, n_wg, n_chunks, w.data(), n, &n);
+  if (rc) return rc;
+  if (n_words) *n_words = n;
+  if (host_out) {
+    if (capacity < n) return fail(MKD_E_INVALID, "host_out too small for the schedule");
+    memcpy(host_out, w.data(), n * 4);
+  }
+  return upload_schedule(m, w.data(), n);
+}
+
+int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_steps,
+               const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev, void* stream) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (!m->d_sched) return fail(MKD_E_INVALID, "no schedule loaded");
+  const mkd_config* c = &m->cfg;
+  if (first_token < 0 || first_token >= c->vocab) return fail(MKD_E_INVALID, "first_token out of range");
+  if (start_pos < 0 || n_steps < 1 || (int64_t)start_pos + n_steps > m->max_seq)
+    return fail(MKD_E_INVALID, "need start_pos >= 0, n_steps >= 1, start_pos + n_steps <= max_seq");
+  if (!tokens_out_dev) return fail(MKD_E_INVALID, "null tokens_out_dev");
+  if (m->trace && m->trace_cap < (size_t)m->n_wg * n_steps * m->max_instr * 2)
+    return fail(MKD_E_INVALID, "trace buffer too small for this launch");
+  if ((int64_t)n_steps * (c->n_layers + 1) >= 0xffffffffll) return fail(MKD_E_INVALID, "n_steps too large");
+  hipError_t e = hipSetDevice(m->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  KParams p{};
+  p.sched = m->d_sched;
+  p.wtab = m->d_wtab;
+  p.kv = m->kv;
+  p.rope = m->d_rope;
+  p.h = m->h; p.qkv = m->qkv; p.part = m->part; p.aout = m->aout;
+  p.hmid = m->hmid; p.act = m->act; p.route = m->route; p.lm = m->lm;
+  p.forced = forced_dev;
+  p.tokens_out = tokens_out_dev;
+  p.logits_out = logits_out_dev;
+  p.status = m->d_status;
+  p.stop = m->h_stop;
+  p.trace = m->trace;
+  p.watchdog_ticks = m->watchdog_ticks;
+  p.n_wg = m->n_wg; p.max_instr = m->max_instr; p.n_chunks = m->n_chunks; p.n_lm_tiles = m->n_lm;
+  p.first_token = first_token; p.start_pos = start_pos; p.n_steps = n_steps; p.max_seq = m->max_seq;
+  p.L = c->n_layers; p.d = c->d_model; p.hq = c->n_q_heads; p.hkv = c->n_kv_heads; p.hd = c->head_dim;
+  p.F = c->d_ff; p.V = c->vocab; p.E = c->n_experts; p.topk = c->top_k;
+  p.qd = c->n_q_heads * c->head_dim; p.kvd = c->n_kv_heads * c->head_dim;
+  p.G = c->n_q_heads / c->n_kv_heads; p.tied = c->tied; p.lslots = layer_slots(c);
+  p.x_floats = m->x_floats;
+  p.out_floats = m->out_floats;
+  p.eps = c->rms_eps;
+  const char* why = "";
+  const int rc = launch(p, m->ll_words, stream, &why);
+  if (rc) return fail(rc, why);
+  if ((e = hipEventRecord(m->done, (hipStream_t)stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  m->launched = true;
+  return MKD_OK;
+}
+
+int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (out) *out = mkd_status{MKD_OK, -1, -1, -1};
+  if (!m->launched) return MKD_OK;
+  hipSetDevice(m->device);
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    const hipError_t q = hipEventQuery(m->done);
+    if (q == hipSuccess) break;
+    if (q != hipErrorNotReady) return hip_fail(q, "launch failed");
+    if (timeout_ms >= 0 &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(timeout_ms))
+      return fail(MKD_E_TIMEOUT, "decode launch still running after the host timeout");
+    std::this_thread::sleep_for(std::chrono::microseconds(200));
+  }
+  int32_t st[S_WORDS];
+  hipError_t e = hipMemcpy(st, m->d_status, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "read status");
+  m->launched = false;
+  __atomic_store_n(m->h_stop, 0, __ATOMIC_SEQ_CST);
+  if (out) *out = mkd_status{st[S_CODE], st[S_WG], st[S_INSTR], st[S_TOKEN]};
+  if (st[S_CODE] != MKD_OK) {
+    return fail(st[S_CODE], "device reported error " + std::to_string(st[S_CODE]) + " at workgroup " +
+                                std::to_string(st[S_WG]) + ", instruction " + std::to_string(st[S_INSTR]) +
+                                ", step " + std::to_string(st[S_TOKEN]));
+  }
+  return MKD_OK;
+}
+
+int mkd_abort(mkd_model* m) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  __atomic_store_n(m->h_stop, 1, __ATOMIC_SEQ_CST);
+  return MKD_OK;
+}
+
+int mkd_set_watchdog(mkd_model* m, int32_t watchdog_ms) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (watchdog_ms < 1) return fail(MKD_E_INVALID, "watchdog_ms must be >= 1");
+  m->watchdog_ticks = (uint64_t)((double)watchdog_ms * 1e-3 * m->clock_hz);
+  return MKD_OK;
+}
+
+int mkd_set_trace(mkd_model* m, uint64_t* trace_dev, size_t capacity_words) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  m->trace = trace_dev;
+  m->trace_cap = trace_dev ? capacity_words : 0;
+  return MKD_OK;
+}
+
+int mkd_clock_hz(mkd_model* m, double* hz) {
+  if (!m || !hz) return fail(MKD_E_INVALID, "null argument");
+  *hz = m->clock_hz;
+  return MKD_OK;
+}
+
+void mkd_destroy(mkd_model* m) {
+  if (!m) return;
+  hipSetDevice(m->device);
+  if (m->launched && m->done) hipEventSynchronize(m->done);
+  if (m->done) hipEventDestroy(m->done);
+  if (m->d_wtab) hipFree(m->d_wtab);
+  if (m->d_rope) hipFree(m->d_rope);
+  if (m->d_status) hipFree(m->d_status);
+  if (m->h_stop) hipHostFree(m->h_stop);
+  if (m->d_ll) hipFree(m->d_ll);
+  if (m->d_sched) hipFree(m->d_sched);
+  delete m;
+}
+
+}  // extern "C"

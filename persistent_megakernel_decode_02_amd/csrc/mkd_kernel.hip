@@ -1,0 +1,1056 @@
+// Persistent batch-1 decode megakernel for gfx950 (MI355X).
+//
+// One cooperative launch; one 512-thread workgroup per compute unit; every
+// workgroup walks its slice of a host-built instruction tensor for every
+// decode step and never exits early (Kittens VM summary, "Method";
+// Hyperkernel teardown, "What a megakernel buys").
+//
+// Synchronisation.  Instead of a separate counter per stage, every value an
+// instruction produces is published as one 64-bit word {fp32 value, 32-bit
+// tag}, stored with an agent-scope atomic store; the tag is the dependency
+// counter of that (step, layer) and a consumer spins on the words it needs
+// until each carries the expected tag.  A 64-bit store is single-copy atomic,
+// so a word with the right tag holds the right value; no release fence or
+// counter round trip sits between a producer's last store and its consumers'
+// first useful load.  The pages' principle of removing fences between
+// pipeline stages (epic-kernel README, "Fence removal and barrier reduction")
+// taken to its end on a device whose L2 is split across 8 XCDs.
+//
+// Weight streaming.  Batch-1 GEMV is one multiply-add per weight, far below
+// the MFMA ridge point, so no matrix cores: each wavefront streams whole rows
+// with coalesced 16-byte (dwordx4) non-temporal loads into a ring of
+// registers, RING loads deep per lane (128 KiB per CU in flight), and issues
+// an instruction's first RING loads *before* waiting on its inputs, so weight
+// traffic overlaps the dependency wait (epic-kernel README, "Pipelining for
+// B200 bandwidth" and "L2 prefetching overlapped with prior instructions";
+// Hyperkernel teardown: next-layer tiles load while the current layer runs).
+// Wavefront reductions use DPP row permutes plus readlane.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "mkd_internal.h"
+
+namespace mkd {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Explicit address spaces: pointers read from the weight table carry none, and
+// generic (flat) accesses would make the compiler wait for every outstanding
+// memory operation, serialising the weight stream.
+#define GLOBAL __attribute__((address_space(1)))
+typedef GLOBAL const u32x4 g_u32x4;
+
+__device__ __forceinline__ u32x4 ld_nt16(const void* p) {
+  return __builtin_nontemporal_load((g_u32x4*)p);
+}
+__device__ __forceinline__ uint16_t ld_u16(const void* p) { return *(GLOBAL const uint16_t*)p; }
+__device__ __forceinline__ float ld_f32(const void* p) { return *(GLOBAL const float*)p; }
+__device__ __forceinline__ int ld_i32(const void* p) { return *(GLOBAL const int*)p; }
+__device__ __forceinline__ uint64_t ld_u64(const void* p) { return *(GLOBAL const uint64_t*)p; }
+__device__ __forceinline__ void st_f32(float* p, float v) { *(GLOBAL float*)p = v; }
+__device__ __forceinline__ void st_i32(int32_t* p, int32_t v) { *(GLOBAL int32_t*)p = v; }
+__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { *(GLOBAL uint64_t*)p = v; }
+
+constexpr int RING = 16;      // 16-byte weight loads in flight per lane (GEMV)
+constexpr int ARING = 4;      // K/V position steps in flight per lane (attention)
+constexpr int kRed = 256;     // LDS floats reserved for reductions
+constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr int kSC1 = 16;                     // cache-policy bit: device-coherent access
+
+// ---------------------------------------------------------------- small helpers
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf_val(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// fp32 -> bf16, round to nearest even (values here are finite)
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ll_store(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// sum over each group of 8 lanes, result in all 8 lanes
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  return v;
+}
+// sum over each row of 16 lanes, result in all 16 lanes
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+// sum over the wavefront, wave-uniform result
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kBufFlags);
+}
+
+// a if !b else c, as integer selects (keeps pointer choices out of memory)
+__device__ __forceinline__ const uint16_t* psel(bool b, const uint16_t* x, const uint16_t* y) {
+  const uint64_t m = 0ull - (uint64_t)b;
+  return (const uint16_t*)(((uint64_t)x & ~m) | ((uint64_t)y & m));
+}
+
+__device__ __forceinline__ uint32_t tag_of(const KParams& p, int t, int l) {
+  return 1u + (uint32_t)t * (uint32_t)(p.L + 1) + (uint32_t)l;
+}
+
+__device__ __forceinline__ const uint16_t* wptr(const KParams& p, int slot) {
+  return (const uint16_t*)ld_u64(p.wtab + slot);
+}
+__device__ __forceinline__ const uint16_t* lptr(const KParams& p, int layer, int slot) {
+  return (const uint16_t*)ld_u64(p.wtab + W_GLOBAL + layer * p.lslots + slot);
+}
+
+// ---------------------------------------------------------------- per-workgroup context
+
+struct Ctx {
+  const KParams& p;
+  float* xs;     // staged input vector   [x_floats]
+  float* res;    // residual rows         [d]
+  float* out;    // GEMV row results      [out_floats]
+  float* red;    // reduction scratch     [kRed]
+  volatile int* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
+  int wg, instr, t, tid, lane, wave;
+};
+
+// Record a device error: the first raiser records where; with stop_all every
+// other workgroup's waits end too.
+__device__ __forceinline__ void raise_at(int32_t* status, volatile int* sflag, int code, bool stop_all,
+                                         int wg, int instr, int t) {
+  int expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&status[S_CODE], &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(&status[S_WG], wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&status[S_INSTR], instr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&status[S_TOKEN], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (stop_all) {
+    __hip_atomic_store(&status[S_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sflag[0] = 1;
+  }
+}
+
+__device__ __forceinline__ void raise_error(Ctx& c, int code, bool stop_all) {
+  raise_at(c.p.status, c.sflag, code, stop_all, c.wg, c.instr, c.t);
+}
+
+// Stage n tagged values src[0..n) into dst (LDS).  Each thread issues its
+// loads first, then spins only on the words that were not yet tagged for this
+// step, polling with backoff until they are, the launch is aborted (stop word,
+// another workgroup's error) or the watchdog deadline passes.  No barrier:
+// callers end a batch of fetches with sync_ok().
+__device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
+  for (int base = 0; base < n; base += kThreads * 4) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kThreads + c.tid;
+      if (i < n) v[u] = ll_load(src + i);
+    }
+    unsigned pending = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kThreads + c.tid;
+      if (i < n) {
+        if ((uint32_t)(v[u] >> 32) == tag) dst[i] = __uint_as_float((uint32_t)v[u]);
+        else pending |= 1u << u;
+      }
+    }
+    if (pending) {
+      const uint64_t t0 = wall_clock64();
+      for (int it = 0; pending; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        for (int u = 0; u < 4; ++u) {
+          if (pending & (1u << u)) {
+            const int i = base + u * kThreads + c.tid;
+            const uint64_t w = ll_load(src + i);
+            if ((uint32_t)(w >> 32) == tag) {
+              dst[i] = __uint_as_float((uint32_t)w);
+              pending &= ~(1u << u);
+            }
+          }
+        }
+        if (pending && (it & 15) == 15) {
+          if (c.sflag[0] ||
+              __hip_atomic_load(&c.p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            c.sflag[0] = 1;
+            break;
+          }
+          if (__hip_atomic_load(c.p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+            raise_error(c, MKD_E_ABORTED, true);
+            break;
+          }
+          if (wall_clock64() - t0 > c.p.watchdog_ticks) {
+            raise_error(c, MKD_E_WATCHDOG, true);
+            break;
+          }
+        }
+      }
+    }
+  }
+}
+
+// workgroup barrier; false when the launch is being aborted
+__device__ __forceinline__ bool sync_ok(Ctx& c) {
+  __syncthreads();
+  const bool ok = c.sflag[0] == 0;
+  return ok;
+}
+
+// sum of v over the workgroup (all threads call; result in all threads)
+__device__ __forceinline__ float block_sum(Ctx& c, float v) {
+  v = wave_sum(v);
+  if (c.lane == 0) c.red[c.wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s += c.red[w];
+  __syncthreads();
+  return s;
+}
+
+// xs[0..d) <- rmsnorm(xs) * gamma  (fp32; gamma bf16)
+__device__ __forceinline__ void rmsnorm_lds(Ctx& c, int d, const uint16_t* gamma) {
+  float ss = 0.f;
+  for (int i = c.tid; i < d; i += kThreads) ss = fmaf(c.xs[i], c.xs[i], ss);
+  const float tot = block_sum(c, ss);
+  const float inv = 1.0f / sqrtf(tot / (float)d + c.p.eps);
+  for (int i = c.tid; i < d; i += kThreads) c.xs[i] = (c.xs[i] * inv) * bf_val(ld_u16(gamma + i));
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- token selection
+
+// (value, index) maximum with the lowest index on ties
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// argmax of step tt's logits from the LM-head tile partials
+__device__ __forceinline__ int fold_argmax(Ctx& c, int tt, bool* ok) {
+  const KParams& p = c.p;
+  const int n = 2 * p.n_lm_tiles;
+  ll_fetch(c, p.lm, n, tag_of(p, tt, p.L), c.xs);
+  if (!sync_ok(c)) { *ok = false; return 0; }
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = c.tid; k < p.n_lm_tiles; k += kThreads) {
+    const float v = c.xs[2 * k];
+    const int i = __float_as_int(c.xs[2 * k + 1]);
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  int* ired = (int*)(c.red + 64);
+  if (c.lane == 0) { c.red[c.wave] = bv; ired[c.wave] = bi; }
+  __syncthreads();
+  bv = c.red[0];
+  bi = ired[0];
+  for (int w = 1; w < kWaves; ++w)
+    if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
+  __syncthreads();
+  *ok = true;
+  return bi;
+}
+
+// token consumed at step t (cached per step in LDS)
+__device__ __forceinline__ int step_token(Ctx& c, bool* ok) {
+  const KParams& p = c.p;
+  *ok = true;
+  if (c.sflag[2] == c.t) return c.sflag[1];
+  int tok;
+  if (c.t == 0) {
+    tok = p.first_token;
+  } else {
+    const int f = p.forced ? ld_i32(p.forced + c.t) : -1;
+    int am = 0;
+    if (f < 0 || c.wg == 0) {
+      am = fold_argmax(c, c.t - 1, ok);
+      if (!*ok) return 0;
+      if (c.wg == 0 && c.tid == 0) st_i32(p.tokens_out + c.t - 1, am);
+    }
+    tok = f >= 0 ? f : am;
+  }
+  if (tok < 0 || tok >= p.V) {
+    if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
+    __syncthreads();
+    *ok = false;
+    return 0;
+  }
+  __syncthreads();
+  if (c.tid == 0) { c.sflag[1] = tok; c.sflag[2] = c.t; }
+  __syncthreads();
+  return tok;
+}
+
+// ---------------------------------------------------------------- GEMV row streamer
+
+// Streams the rows of one instruction through a per-wavefront register ring.
+// Row k of this wavefront's stream is m.row(k) (K bf16 values), dotted with
+// xs[m.xoff(k) .. + K); the result goes to the LDS slot m.slot(k).  Every
+// ring refill is issued unconditionally -- slots past the end of the stream
+// read one shared 16-byte word (an L1 hit) -- and nothing else touches
+// global memory inside the loop, so the compiler can wait for exactly the
+// oldest load instead of draining the ring.
+template <class Map>
+struct RowStream {
+  const Map& m;
+  const int K, nseg, S, lane;
+  int pk, pseg, ps;
+  const u32x4* prow;
+  const u32x4* dummy;
+  u32x4 ring[RING];
+
+  __device__ __forceinline__ RowStream(const Map& m_, int K_, int nrows, int lane_, const void* dummy_)
+      : m(m_), K(K_), nseg((K_ + 511) >> 9), S(nrows * ((K_ + 511) >> 9)), lane(lane_), pk(0), pseg(0),
+        ps(0), dummy((const u32x4*)dummy_) {
+    prow = nrows > 0 ? (const u32x4*)m.row(0) : dummy;
+  }
+  __device__ __forceinline__ u32x4 next() {
+    // lanes past the row end (K not a multiple of 512) re-read the row's
+    // first 16 bytes and are skipped by the consumer
+    const int ch = pseg * 64 + lane;
+    const u32x4* a = ps < S ? prow + (ch * 8 < K ? ch : 0) : dummy;
+    const u32x4 v = ld_nt16(a);
+    ++ps;
+    if (++pseg == nseg) {
+      pseg = 0;
+      ++pk;
+      if (ps < S) prow = (const u32x4*)m.row(pk);
+    }
+    return v;
+  }
+  __device__ __forceinline__ void prefetch() {
+#pragma unroll
+    for (int d = 0; d < RING; ++d) ring[d] = next();
+  }
+  __device__ __forceinline__ void run(const float* xs, float* out) {
+    int ck = 0, cseg = 0;
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int s0 = 0; s0 < S; s0 += RING) {
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        if (s0 + d < S) {
+          const int ch = cseg * 64 + lane;
+          if (ch * 8 < K) {
+            const float* xp = xs + m.xoff(ck) + ch * 8;
+            const f32x4 a = *(const f32x4*)xp;
+            const f32x4 b = *(const f32x4*)(xp + 4);
+            const u32x4 w = ring[d];
+            acc0 = fmaf(bf_lo(w.x), a.x, acc0);
+            acc1 = fmaf(bf_hi(w.x), a.y, acc1);
+            acc0 = fmaf(bf_lo(w.y), a.z, acc0);
+            acc1 = fmaf(bf_hi(w.y), a.w, acc1);
+            acc0 = fmaf(bf_lo(w.z), b.x, acc0);
+            acc1 = fmaf(bf_hi(w.z), b.y, acc1);
+            acc0 = fmaf(bf_lo(w.w), b.z, acc0);
+            acc1 = fmaf(bf_hi(w.w), b.w, acc1);
+          }
+          if (++cseg == nseg) {
+            const float v = wave_sum(acc0 + acc1);
+            if (lane == 0) out[m.slot(ck)] = v;
+            acc0 = 0.f;
+            acc1 = 0.f;
+            cseg = 0;
+            ++ck;
+          }
+        }
+        ring[d] = next();
+      }
+    }
+  }
+};
+
+// rows of a tile handled by wavefront w: local rows w, w + kWaves, ...
+__device__ __forceinline__ int wave_rows(int nrows, int w) {
+  return nrows > w ? (nrows - w + kWaves - 1) / kWaves : 0;
+}
+
+// one matrix, rows [a, b) of row length K; slot = local row
+struct PlainMap {
+  const uint16_t* W;
+  int a, w, K;
+  __device__ const uint16_t* row(int k) const { return W + (size_t)(a + w + k * kWaves) * K; }
+  __device__ int xoff(int) const { return 0; }
+  __device__ int slot(int k) const { return w + k * kWaves; }
+};
+
+// two matrices interleaved per local row i: streamed row 2i from X, 2i+1 from
+// Y (x offset xo for Y); slots 2i and 2i+1
+struct PairMap {
+  const uint16_t *X, *Y;
+  int a, w, K, yoff;
+  __device__ const uint16_t* row(int k) const {
+    return psel(k & 1, X, Y) + (size_t)(a + w + (k >> 1) * kWaves) * K;
+  }
+  __device__ int xoff(int k) const { return (k & 1) ? yoff : 0; }
+  __device__ int slot(int k) const { return 2 * (w + (k >> 1) * kWaves) + (k & 1); }
+};
+
+// ---------------------------------------------------------------- opcode: RMSNorm + QKV
+
+struct QkvMap {
+  const uint16_t *wq, *wk, *wv;
+  int a, w, d, qd, kvd;
+  __device__ const uint16_t* row(int k) const {
+    const int r = a + w + k * kWaves;
+    const bool isk = r >= qd, isv = r >= qd + kvd;
+    const int rr = r - (isk ? qd : 0) - (isv ? kvd : 0);
+    return psel(isk, wq, psel(isv, wk, wv)) + (size_t)rr * d;
+  }
+  __device__ int xoff(int) const { return 0; }
+  __device__ int slot(int k) const { return w + k * kWaves; }
+};
+
+// stage the residual entering layer l (the embedding at layer 0) into dst
+// for rows [r0, r1); false on abort
+__device__ __forceinline__ bool fetch_hin(Ctx& c, int l, int r0, int r1, float* dst) {
+  const KParams& p = c.p;
+  if (l == 0) {
+    bool ok;
+    const int tok = step_token(c, &ok);
+    if (!ok) return false;
+    const uint16_t* e = wptr(p, W_EMBED) + (size_t)tok * p.d;
+    for (int i = r0 + c.tid; i < r1; i += kThreads) dst[i - r0] = bf_val(ld_u16(e + i));
+  } else {
+    ll_fetch(c, p.h + r0, r1 - r0, tag_of(p, c.t, l), dst);
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool op_qkv(Ctx& c, int l, int a, int b) {
+  const KParams& p = c.p;
+  const QkvMap m{lptr(p, l, WL_Q), lptr(p, l, WL_K), lptr(p, l, WL_V), a, c.wave, p.d, p.qd, p.kvd};
+  RowStream<QkvMap> rs(m, p.d, wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  if (!fetch_hin(c, l, 0, p.d, c.xs)) return false;
+  if (!sync_ok(c)) return false;
+  rmsnorm_lds(c, p.d, lptr(p, l, WL_ATTN_NORM));
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  const uint32_t tag = tag_of(p, c.t, l);
+  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.qkv + a + i, c.out[i], tag);
+  return true;
+}
+
+// ---------------------------------------------------------------- opcode: O-proj + residual
+
+__device__ __forceinline__ bool op_oproj(Ctx& c, int l, int a, int b) {
+  const KParams& p = c.p;
+  const PlainMap m{lptr(p, l, WL_O), a, c.wave, p.qd};
+  RowStream<PlainMap> rs(m, p.qd, wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  if (!fetch_hin(c, l, a, b, c.res)) return false;
+  ll_fetch(c, p.aout, p.qd, tag_of(p, c.t, l), c.xs);
+  if (!sync_ok(c)) return false;
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  const uint32_t tag = tag_of(p, c.t, l);
+  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.hmid + a + i, c.res[i] + c.out[i], tag);
+  return true;
+}
+
+// ---------------------------------------------------------------- opcode: RMSNorm + up/gate + SiLU
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ bool op_upgate(Ctx& c, int l, int a, int b) {
+  const KParams& p = c.p;
+  const PairMap m{lptr(p, l, WL_GATE), lptr(p, l, WL_UP), a, c.wave, p.d, 0};
+  RowStream<PairMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  ll_fetch(c, p.hmid, p.d, tag_of(p, c.t, l), c.xs);
+  if (!sync_ok(c)) return false;
+  rmsnorm_lds(c, p.d, lptr(p, l, WL_FFN_NORM));
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  const uint32_t tag = tag_of(p, c.t, l);
+  for (int i = c.tid; i < b - a; i += kThreads)
+    ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
+  return true;
+}
+
+// ---------------------------------------------------------------- opcode: down + residual
+
+__device__ __forceinline__ bool op_down(Ctx& c, int l, int a, int b) {
+  const KParams& p = c.p;
+  const PlainMap m{lptr(p, l, WL_DOWN), a, c.wave, p.F};
+  RowStream<PlainMap> rs(m, p.F, wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  ll_fetch(c, p.hmid + a, b - a, tag_of(p, c.t, l), c.res);
+  ll_fetch(c, p.act, p.F, tag_of(p, c.t, l), c.xs);
+  if (!sync_ok(c)) return false;
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  const uint32_t tag = tag_of(p, c.t, l + 1);
+  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.h + a + i, c.res[i] + c.out[i], tag);
+  return true;
+}
+
+// ---------------------------------------------------------------- opcodes: MoE
+
+// expert-rows r in [a, b) of the top_k * F stacked rows: r < F is expert a's
+// row r, else expert b's row r - F; streamed rows alternate gate and up
+struct MoeUpMap {
+  const uint16_t *ga, *ua, *gb, *ub;
+  int a, w, d, F;
+  __device__ const uint16_t* row(int k) const {
+    const int r = a + w + (k >> 1) * kWaves;
+    const bool second = r >= F;
+    const int rr = second ? r - F : r;
+    return psel(k & 1, psel(second, ga, gb), psel(second, ua, ub)) + (size_t)rr * d;
+  }
+  __device__ int xoff(int) const { return 0; }
+  __device__ int slot(int k) const { return 2 * (w + (k >> 1) * kWaves) + (k & 1); }
+};
+
+__device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int index) {
+  const KParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, l);
+  ll_fetch(c, p.hmid, p.d, tag, c.xs);
+  if (!sync_ok(c)) return false;
+  rmsnorm_lds(c, p.d, lptr(p, l, WL_FFN_NORM));
+  // router logits: one wavefront per expert row
+  const uint16_t* wr = lptr(p, l, WL_ROUTER);
+  for (int e = c.wave; e < p.E; e += kWaves) {
+    float acc = 0.f;
+    for (int i = c.lane; i < p.d; i += 64) acc = fmaf(bf_val(ld_u16(wr + (size_t)e * p.d + i)), c.xs[i], acc);
+    const float z = wave_sum(acc);
+    if (c.lane == 0) c.red[64 + e] = z;
+  }
+  __syncthreads();
+  if (c.tid == 0) {
+    // top-2: larger logit first, lower expert index on ties
+    int ea = 0;
+    for (int e = 1; e < p.E; ++e)
+      if (c.red[64 + e] > c.red[64 + ea]) ea = e;
+    int eb = ea == 0 ? 1 : 0;
+    for (int e = 0; e < p.E; ++e)
+      if (e != ea && c.red[64 + e] > c.red[64 + eb]) eb = e;
+    const float za = c.red[64 + ea], zb = c.red[64 + eb];
+    const float q = expf(zb - za);
+    c.sflag[3] = ea;
+    c.sflag[4] = eb;
+    if (index == 0) {
+      ll_store(p.route + 0, __int_as_float(ea), tag);
+      ll_store(p.route + 1, __int_as_float(eb), tag);
+      ll_store(p.route + 2, 1.0f / (1.0f + q), tag);
+      ll_store(p.route + 3, q / (1.0f + q), tag);
+    }
+  }
+  __syncthreads();
+  const int ea = c.sflag[3], eb = c.sflag[4];
+  const MoeUpMap m{lptr(p, l, WL_EXPERTS + ea), lptr(p, l, WL_EXPERTS + p.E + ea),
+                   lptr(p, l, WL_EXPERTS + eb), lptr(p, l, WL_EXPERTS + p.E + eb), a, c.wave, p.d, p.F};
+  RowStream<MoeUpMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  for (int i = c.tid; i < b - a; i += kThreads)
+    ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
+  return true;
+}
+
+__device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
+  const KParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, l);
+  ll_fetch(c, p.route, 4, tag, c.red + 8);
+  ll_fetch(c, p.hmid + a, b - a, tag, c.res);
+  ll_fetch(c, p.act, 2 * p.F, tag, c.xs);
+  if (!sync_ok(c)) return false;
+  const int ea = __float_as_int(c.red[8]), eb = __float_as_int(c.red[9]);
+  const float wa = c.red[10], wb = c.red[11];
+  if (ea < 0 || ea >= p.E || eb < 0 || eb >= p.E) {
+    if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
+    __syncthreads();
+    return false;
+  }
+  const PairMap m{lptr(p, l, WL_EXPERTS + 2 * p.E + ea), lptr(p, l, WL_EXPERTS + 2 * p.E + eb), a,
+                  c.wave, p.F, p.F};
+  RowStream<PairMap> rs(m, p.F, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  const uint32_t otag = tag_of(p, c.t, l + 1);
+  for (int i = c.tid; i < b - a; i += kThreads)
+    ll_store(p.h + a + i, c.res[i] + (wa * c.out[2 * i] + wb * c.out[2 * i + 1]), otag);
+  return true;
+}
+
+// ---------------------------------------------------------------- opcode: LM head
+
+__device__ __forceinline__ bool op_lmhead(Ctx& c, int a, int b, int index) {
+  const KParams& p = c.p;
+  const PlainMap m{wptr(p, p.tied ? W_EMBED : W_LM_HEAD), a, c.wave, p.d};
+  RowStream<PlainMap> rs(m, p.d, wave_rows(b - a, c.wave), c.lane, p.sched);
+  rs.prefetch();
+  ll_fetch(c, p.h, p.d, tag_of(p, c.t, p.L), c.xs);
+  if (!sync_ok(c)) return false;
+  rmsnorm_lds(c, p.d, wptr(p, W_FINAL_NORM));
+  rs.run(c.xs, c.out);
+  __syncthreads();
+  float* logits = p.logits_out ? p.logits_out + (size_t)c.t * p.V + a : nullptr;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  int fin = 1;
+  for (int i = c.tid; i < b - a; i += kThreads) {
+    const float v = c.out[i];
+    if (logits) st_f32(logits + i, v);
+    fin &= isfinite(v) ? 1 : 0;
+    if (better(v, a + i, bv, bi)) { bv = v; bi = a + i; }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    fin &= __shfl_xor(fin, off);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  int* ired = (int*)(c.red + 64);
+  if (c.lane == 0) {
+    c.red[c.wave] = bv;
+    ired[c.wave] = bi;
+    ired[16 + c.wave] = fin;
+  }
+  __syncthreads();
+  if (c.tid == 0) {
+    bv = c.red[0];
+    bi = ired[0];
+    bool all_fin = ired[16] != 0;
+    for (int w = 1; w < kWaves; ++w) {
+      if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
+      all_fin = all_fin && ired[16 + w] != 0;
+    }
+    if (!all_fin) raise_error(c, MKD_E_NONFINITE, false);
+    const uint32_t tag = tag_of(p, c.t, p.L);
+    ll_store(p.lm + 2 * index, bv, tag);
+    ll_store(p.lm + 2 * index + 1, __int_as_float(bi), tag);
+  }
+  __syncthreads();
+  return true;
+}
+
+// ---------------------------------------------------------------- opcode: RoPE + KV append + attention
+
+// online-softmax state of one lane group for G heads (log2 domain)
+template <int G>
+struct AttnState {
+  float m[G], l[G], o[G][8];
+};
+
+template <int G>
+__device__ __forceinline__ void merge_into(AttnState<G>& s, const float* om, const float* ol,
+                                           const float (*oo)[8]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float M = fmaxf(s.m[g], om[g]);
+    if (M == -INFINITY) continue;
+    const float a1 = exp2f(s.m[g] - M), a2 = exp2f(om[g] - M);
+    s.l[g] = s.l[g] * a1 + ol[g] * a2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.o[g][i] = s.o[g][i] * a1 + oo[g][i] * a2;
+    s.m[g] = M;
+  }
+}
+
+template <int HD, int G>
+__device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
+  const KParams& p = c.p;
+  constexpr int LPR = HD / 8;     // lanes per K/V row
+  constexpr int PPW = 64 / LPR;   // positions per wavefront load
+  const int pos = p.start_pos + c.t;
+  const int T = pos + 1;
+  const int clen = ((T + p.n_chunks - 1) / p.n_chunks + 15) / 16 * 16;
+  const int lo = min(T, chunk * clen), hi = min(T, (chunk + 1) * clen);
+  const int hic = min(hi, pos);             // cached positions [lo, hic)
+  const bool has_new = lo <= pos && pos < hi;
+  const int grp = c.lane / LPR, sub = c.lane % LPR;
+
+  const size_t head_elems = (size_t)p.max_seq * HD;
+  const uint16_t* kb = p.kv + ((size_t)(l * 2 + 0) * p.hkv + kvh) * head_elems;
+  const uint16_t* vb = p.kv + ((size_t)(l * 2 + 1) * p.hkv + kvh) * head_elems;
+  const uint32_t hbytes = (uint32_t)(head_elems * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, hbytes), vr = make_rsrc(vb, hbytes);
+
+  // this wavefront's position blocks: wave, wave + kWaves, ... ; block j covers
+  // positions lo + j*PPW + [0, PPW), lane group grp takes one of them
+  const int nblk = hic > lo ? (hic - lo + PPW - 1) / PPW : 0;
+  const int nsteps = nblk > c.wave ? (nblk - c.wave + kWaves - 1) / kWaves : 0;
+  u32x4 rk[ARING], rv[ARING];
+  int pstep = 0;
+  // positions past the chunk use an offset beyond the buffer range: the load
+  // returns zeros without touching memory, so every issue is unconditional
+  auto issue = [&](u32x4& k_, u32x4& v_) {
+    const int j = lo + (c.wave + pstep * kWaves) * PPW + grp;
+    const int off = j < hic ? (j * HD + sub * 8) * 2 : 0x7ffffff0;
+    k_ = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, kSC1);
+    v_ = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, kSC1);
+    ++pstep;
+  };
+#pragma unroll
+  for (int d = 0; d < ARING; ++d) issue(rk[d], rv[d]);
+
+  // inputs: raw q of the G heads, k and v of this kv head
+  float* qs = c.xs;                 // [G][HD]
+  float* ks = c.xs + G * HD;        // [HD]
+  float* vs = ks + HD;              // [HD]
+  float* wst = vs + HD;             // [kWaves][G][HD + 2] per-wave states
+  const uint32_t tag = tag_of(p, c.t, l);
+  ll_fetch(c, p.qkv + kvh * G * HD, G * HD, tag, qs);
+  ll_fetch(c, p.qkv + p.qd + kvh * HD, HD, tag, ks);
+  ll_fetch(c, p.qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs);
+  if (!sync_ok(c)) return false;
+
+  // RoPE (pairs i, i + HD/2) on q heads and k; q pre-scaled for exp2 softmax
+  const float* cosr = p.rope + (size_t)pos * (HD / 2);
+  const float* sinr = p.rope + (size_t)p.max_seq * (HD / 2) + (size_t)pos * (HD / 2);
+  const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+  for (int e = c.tid; e < (G + 1) * (HD / 2); e += kThreads) {
+    const int h = e / (HD / 2), i = e % (HD / 2);
+    float* x = h < G ? qs + h * HD : ks;
+    const float cs = ld_f32(cosr + i), sn = ld_f32(sinr + i);
+    const float x0 = x[i], x1 = x[i + HD / 2];
+    float y0 = x0 * cs - x1 * sn;
+    float y1 = x1 * cs + x0 * sn;
+    if (h < G) {
+      y0 *= qscale;
+      y1 *= qscale;
+    } else {
+      y0 = __uint_as_float(to_bf16(y0) << 16);
+      y1 = __uint_as_float(to_bf16(y1) << 16);
+    }
+    x[i] = y0;
+    x[i + HD / 2] = y1;
+  }
+  for (int i = c.tid; i < HD; i += kThreads) vs[i] = __uint_as_float(to_bf16(vs[i]) << 16);
+  __syncthreads();
+
+  // append K and V at pos (the chunk holding pos owns it)
+  if (has_new && c.tid < LPR) {
+    u32x4 kw, vw;
+    const float* kk = ks + c.tid * 8;
+    const float* vv = vs + c.tid * 8;
+    kw.x = to_bf16(kk[0]) | (to_bf16(kk[1]) << 16);
+    kw.y = to_bf16(kk[2]) | (to_bf16(kk[3]) << 16);
+    kw.z = to_bf16(kk[4]) | (to_bf16(kk[5]) << 16);
+    kw.w = to_bf16(kk[6]) | (to_bf16(kk[7]) << 16);
+    vw.x = to_bf16(vv[0]) | (to_bf16(vv[1]) << 16);
+    vw.y = to_bf16(vv[2]) | (to_bf16(vv[3]) << 16);
+    vw.z = to_bf16(vv[4]) | (to_bf16(vv[5]) << 16);
+    vw.w = to_bf16(vv[6]) | (to_bf16(vv[7]) << 16);
+    const int off = (pos * HD + c.tid * 8) * 2;
+    __builtin_amdgcn_raw_buffer_store_b128(kw, kr, off, 0, kSC1);
+    __builtin_amdgcn_raw_buffer_store_b128(vw, vr, off, 0, kSC1);
+  }
+
+  // q slices of this lane
+  float q[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[g][i] = qs[g * HD + sub * 8 + i];
+
+  AttnState<G> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[g][i] = 0.f;
+  }
+
+  for (int s0 = 0; s0 < nsteps; s0 += ARING) {
+#pragma unroll
+    for (int d = 0; d < ARING; ++d) {
+      if (s0 + d < nsteps) {
+        const int j = lo + (c.wave + (s0 + d) * kWaves) * PPW + grp;
+        const u32x4 kw = rk[d], vw = rv[d];
+        float kf[8], vf[8];
+        kf[0] = bf_lo(kw.x); kf[1] = bf_hi(kw.x); kf[2] = bf_lo(kw.y); kf[3] = bf_hi(kw.y);
+        kf[4] = bf_lo(kw.z); kf[5] = bf_hi(kw.z); kf[6] = bf_lo(kw.w); kf[7] = bf_hi(kw.w);
+        vf[0] = bf_lo(vw.x); vf[1] = bf_hi(vw.x); vf[2] = bf_lo(vw.y); vf[3] = bf_hi(vw.y);
+        vf[4] = bf_lo(vw.z); vf[5] = bf_hi(vw.z); vf[6] = bf_lo(vw.w); vf[7] = bf_hi(vw.w);
+
+        const bool valid = j < hic;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s = fmaf(q[g][i], kf[i], s);
+          s = (LPR == 8) ? sum8(s) : sum16(s);
+          if (valid) {
+            const float M = fmaxf(st.m[g], s);
+            const float a = exp2f(st.m[g] - M), e = exp2f(s - M);
+            st.l[g] = st.l[g] * a + e;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st.o[g][i] = fmaf(st.o[g][i], a, e * vf[i]);
+            st.m[g] = M;
+          }
+        }
+      }
+      issue(rk[d], rv[d]);
+    }
+  }
+
+  // merge the lane groups of this wavefront (xor over group bits)
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    float om[G], ol[G], oo[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      om[g] = __shfl_xor(st.m[g], off);
+      ol[g] = __shfl_xor(st.l[g], off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) oo[g][i] = __shfl_xor(st.o[g][i], off);
+    }
+    merge_into<G>(st, om, ol, oo);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* ws = wst + (c.wave * G + g) * (HD + 2);
+      if (sub == 0) { ws[0] = st.m[g]; ws[1] = st.l[g]; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[2 + sub * 8 + i] = st.o[g][i];
+    }
+  }
+  // the appended K/V must be visible device-wide before anything that
+  // depends on this instruction can run: the storing wavefront waits for its
+  // stores to complete before the barrier that precedes the output stores
+  if (has_new && c.wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // score of the new position (one per head)
+  __syncthreads();
+  float* pnew = c.red;  // [G] new-position scores
+  if (has_new && c.tid < G) {
+    float s = 0.f;
+    for (int i = 0; i < HD; ++i) s = fmaf(qs[c.tid * HD + i], ks[i], s);
+    pnew[c.tid] = s;
+  }
+  __syncthreads();
+
+  // final merge over wavefronts (fixed order) and the new position; one
+  // thread per (head, element)
+  const uint32_t otag = tag;
+  for (int e = c.tid; e < G * HD; e += kThreads) {
+    const int g = e / HD, i = e % HD;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wst[(w * G + g) * (HD + 2)]);
+    if (has_new) M = fmaxf(M, pnew[g]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float* ws = wst + (w * G + g) * (HD + 2);
+        const float a = exp2f(ws[0] - M);
+        L = fmaf(ws[1], a, L);
+        O = fmaf(ws[2 + i], a, O);
+      }
+      if (has_new) {
+        const float a = exp2f(pnew[g] - M);
+        L += a;
+        O = fmaf(vs[i], a, O);
+      }
+    }
+    const int qh = kvh * G + g;
+    if (p.n_chunks == 1) {
+      ll_store(p.aout + qh * HD + i, O / L, otag);
+    } else {
+      uint64_t* pp = p.part + ((size_t)qh * p.n_chunks + chunk) * (HD + 2);
+      ll_store(pp + 2 + i, O, otag);
+      if (i == 0) {
+        ll_store(pp + 0, M, otag);
+        ll_store(pp + 1, L, otag);
+      }
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+template <int HD>
+__device__ __forceinline__ bool op_attn_hd(Ctx& c, int l, int kvh, int chunk) {
+  switch (c.p.G) {
+    case 1: return op_attn_t<HD, 1>(c, l, kvh, chunk);
+    case 2: return op_attn_t<HD, 2>(c, l, kvh, chunk);
+    case 3: return op_attn_t<HD, 3>(c, l, kvh, chunk);
+    default: return op_attn_t<HD, 4>(c, l, kvh, chunk);
+  }
+}
+
+// ---------------------------------------------------------------- opcode: split-KV reduction
+
+__device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
+  const KParams& p = c.p;
+  const int HD = p.hd, n = p.n_chunks, W = HD + 2;
+  const uint32_t tag = tag_of(p, c.t, l);
+  ll_fetch(c, p.part + (size_t)qh * n * W, n * W, tag, c.xs);
+  if (!sync_ok(c)) return false;
+  for (int i = c.tid; i < HD; i += kThreads) {
+    float M = -INFINITY;
+    for (int k = 0; k < n; ++k) M = fmaxf(M, c.xs[k * W]);
+    float L = 0.f, O = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const float a = exp2f(c.xs[k * W] - M);
+      L = fmaf(c.xs[k * W + 1], a, L);
+      O = fmaf(c.xs[k * W + 2 + i], a, O);
+    }
+    ll_store(p.aout + qh * HD + i, O / L, tag);
+  }
+  __syncthreads();
+  return true;
+}
+
+// ---------------------------------------------------------------- the kernel
+
+__shared__ int s_flags[8];
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams params) {
+  // The parameters are read in place in the kernel-argument segment (they
+  // are the first and only argument): referring to the by-value parameter
+  // itself would make the compiler copy it to scratch memory.
+  (void)params;
+  const KParams* pk = (const KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  extern __shared__ __align__(16) float smem[];
+  volatile int* sflag = s_flags;
+  const int wg = blockIdx.x;
+  if (threadIdx.x == 0) {
+    sflag[0] = 0;
+    sflag[1] = 0;
+    sflag[2] = -1;
+  }
+  __syncthreads();
+  const int n = ld_i32(pk->sched + kWords + wg);
+  bool ok = true;
+  for (int t = 0; t < pk->n_steps && ok; ++t) {
+    for (int i = 0; i < n && ok; ++i) {
+      // Opaque copies of the parameter pointer and thread id: nothing that
+      // depends on them is hoisted out of the persistent loop, so values one
+      // opcode needs do not stay live (and spill) through all the others.
+      const KParams* pp = pk;
+      int tid = threadIdx.x;
+      asm volatile("" : "+s"(pp));
+      asm volatile("" : "+v"(tid));
+      const KParams& p = *pp;
+      Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
+            sflag, wg, i, t, tid, tid & 63, tid >> 6};
+      const int32_t* ins = p.sched + kWords + p.n_wg + ((size_t)wg * p.max_instr + i) * kWords;
+      const int op = ld_i32(ins + I_OP), l = ld_i32(ins + I_LAYER), a = ld_i32(ins + I_A),
+                b = ld_i32(ins + I_B), index = ld_i32(ins + I_INDEX);
+      uint64_t* tr = p.trace ? p.trace + (((size_t)wg * p.n_steps + t) * p.max_instr + i) * 2 : nullptr;
+      if (tr && tid == 0) st_u64(tr, wall_clock64());
+      switch (op) {
+        case OP_QKV: ok = op_qkv(c, l, a, b); break;
+        case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
+        case OP_AREDUCE: ok = op_areduce(c, l, a); break;
+        case OP_OPROJ: ok = op_oproj(c, l, a, b); break;
+        case OP_UPGATE: ok = op_upgate(c, l, a, b); break;
+        case OP_DOWN: ok = op_down(c, l, a, b); break;
+        case OP_MOE_UPGATE: ok = op_moe_upgate(c, l, a, b, index); break;
+        case OP_MOE_DOWN: ok = op_moe_down(c, l, a, b); break;
+        case OP_LMHEAD: ok = op_lmhead(c, a, b, index); break;
+        default: break;
+      }
+      if (tr && tid == 0) st_u64(tr + 1, wall_clock64());
+    }
+  }
+  // the last step's argmax
+  if (ok && wg == 0) {
+    const KParams& p = *pk;
+    const int tid = threadIdx.x;
+    Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
+          sflag, wg, 0, p.n_steps, tid, tid & 63, tid >> 6};
+    bool fok;
+    const int am = fold_argmax(c, p.n_steps - 1, &fok);
+    if (fok && tid == 0) st_i32(p.tokens_out + p.n_steps - 1, am);
+  }
+}
+
+extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) ll[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < S_WORDS) {
+    const int k = threadIdx.x;
+    status[k] = (k == S_WG || k == S_INSTR || k == S_TOKEN) ? -1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- host-side launch
+
+size_t lds_bytes(const KParams& p) {
+  return ((size_t)p.x_floats + (size_t)p.d + (size_t)p.out_floats + kRed) * sizeof(float);
+}
+
+int max_coop_blocks(int device, size_t lds, int* out) {
+  if (hipSetDevice(device) != hipSuccess) return MKD_E_HIP;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)mkd_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return MKD_E_HIP;
+  int per_cu = 0, n_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)mkd_megakernel, kThreads,
+                                                   lds) != hipSuccess)
+    return MKD_E_HIP;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return MKD_E_HIP;
+  *out = per_cu * n_cu;
+  return MKD_OK;
+}
+
+int launch(const KParams& p, size_t ll_words, void* stream, const char** why) {
+  hipStream_t s = (hipStream_t)stream;
+  const size_t lds = lds_bytes(p);
+  int blocks = (int)((ll_words + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(mkd_reset, dim3(blocks), dim3(256), 0, s, p.h, ll_words, p.status);
+  if (hipGetLastError() != hipSuccess) { *why = "reset kernel launch failed"; return MKD_E_HIP; }
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)mkd_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess) {
+    *why = "cannot raise the kernel's LDS limit";
+    return MKD_E_HIP;
+  }
+  KParams pc = p;
+  void* args[] = {&pc};
+  const hipError_t e = hipLaunchCooperativeKernel((const void*)mkd_megakernel, dim3(p.n_wg),
+                                                  dim3(kThreads), args, (unsigned)lds, s);
+  if (e == hipErrorCooperativeLaunchTooLarge) {
+    *why = "grid does not fit co-resident on the device";
+    return MKD_E_COOPERATIVE;
+  }
+  if (e != hipSuccess) {
+    *why = hipGetErrorString(e);
+    return MKD_E_HIP;
+  }
+  return MKD_OK;
+}
+
+}  // namespace mkd

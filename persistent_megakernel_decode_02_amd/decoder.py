@@ -1,0 +1,80 @@
+"""Keeps the torch tensors a libmkd handle borrows alive, and turns calls into
+the C ABI's (argument marshalling only; all compute runs in the library)."""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import capi
+
+
+class Decoder:
+    """One model on one GPU: weights (bf16 device tensors in pointer order),
+    a bf16 KV cache tensor, and the library handle with a loaded schedule."""
+
+    def __init__(self, cfg, weights: Sequence[torch.Tensor], kv_cache: torch.Tensor, max_seq: int,
+                 n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None):
+        self.cfg = cfg
+        self.ccfg = capi.make_config(cfg)
+        self.weights = list(weights)
+        self.kv = kv_cache
+        self.max_seq = max_seq
+        self.device = kv_cache.device.index if device is None else device
+        for i, w in enumerate(self.weights):
+            r, c = capi.mkd_weight_shape(self.ccfg, i)
+            if w.dtype != torch.bfloat16 or not w.is_contiguous() or w.numel() != r * c:
+                raise ValueError(f"weight {i}: expected contiguous bf16 with {r}x{c} elements")
+        if kv_cache.dtype != torch.bfloat16 or not kv_cache.is_contiguous():
+            raise ValueError("kv cache must be contiguous bf16")
+        if kv_cache.numel() * 2 != capi.mkd_kv_cache_bytes(self.ccfg, max_seq):
+            raise ValueError("kv cache size does not match max_seq")
+        self.handle = capi.mkd_init(self.ccfg, self.weights, kv_cache, max_seq, self.device)
+        self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
+
+    @property
+    def n_wg(self) -> int:
+        return int(self.schedule[2])
+
+    @property
+    def n_chunks(self) -> int:
+        return int(self.schedule[5])
+
+    @property
+    def max_instr(self) -> int:
+        return int(self.schedule[4])
+
+    def rebuild(self, n_wg: int = 0, n_chunks: int = 0) -> None:
+        self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
+
+    def launch(self, first_token: int, start_pos: int, n_steps: int, tokens_out: torch.Tensor,
+               logits_out: Optional[torch.Tensor] = None, forced: Optional[torch.Tensor] = None,
+               stream=None) -> None:
+        """Enqueue one decode launch (asynchronous)."""
+        capi.mkd_decode(self.handle, first_token, start_pos, n_steps, tokens_out, logits_out, forced,
+                        stream)
+
+    def decode(self, first_token: int, start_pos: int, n_steps: int, want_logits: bool = True,
+               forced: Optional[Sequence[int]] = None, timeout_ms: int = 120000):
+        """Run one launch and wait: (tokens [n] int32, logits [n, V] float32 or None)."""
+        dev = self.kv.device
+        toks = torch.empty(n_steps, dtype=torch.int32, device=dev)
+        logits = torch.empty(n_steps, self.cfg.vocab, dtype=torch.float32, device=dev) if want_logits else None
+        f = None
+        if forced is not None:
+            f = torch.tensor(list(forced), dtype=torch.int32, device=dev)
+        self.launch(first_token, start_pos, n_steps, toks, logits, f)
+        capi.mkd_wait(self.handle, timeout_ms)
+        torch.cuda.synchronize(dev)
+        return toks, logits
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            capi.mkd_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,104 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and its host logic (config checks, weight shapes, the schedule
+builder and validator) agrees with the oracle -- no GPU calls."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import schedule as S
+from persistent_megakernel_decode_02_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mkd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(capi.LIB_PATH), reason="libmkd.so not built")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mkd_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    lib = capi.load()
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(capi.EXPORTS) == declared
+
+
+def test_version():
+    assert capi.mkd_version() == 1
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "llama3b", "mixtral"])
+def test_weight_count_and_shapes_match_specs(name):
+    cfg = synth.PRESETS[name]
+    c = capi.make_config(cfg)
+    specs = synth.weight_specs(cfg)
+    assert capi.mkd_weight_count(c) == len(specs)
+    for i, (n, shape) in enumerate(specs):
+        r, k = capi.mkd_weight_shape(c, i)
+        assert (r, k) == (shape[0], shape[1] if len(shape) == 2 else 1), n
+
+
+def test_kv_bytes():
+    cfg = synth.PRESETS["llama1b"]
+    assert capi.mkd_kv_cache_bytes(capi.make_config(cfg), 4096) == 16 * 2 * 8 * 4096 * 64 * 2
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("n_kv_heads", 3), ("d_model", 250),
+                                          ("top_k", 1), ("n_layers", 0), ("vocab", 0)])
+def test_config_check_rejects(field, value):
+    c = capi.make_config(synth.PRESETS["tiny"])
+    setattr(c, field, value)
+    with pytest.raises(capi.MkdError) as e:
+        capi.mkd_config_check(c)
+    assert e.value.code == capi.MKD_E_INVALID
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "llama3b", "mixtral"])
+@pytest.mark.parametrize("n_wg", [1, 3, 8, 64, 256, 304])
+def test_schedule_bit_exact_with_oracle(name, n_wg):
+    cfg = synth.PRESETS[name]
+    c = capi.make_config(cfg)
+    for n_chunks in (1, 4, 32):
+        got = capi.mkd_schedule_build(c, n_wg, n_chunks)
+        want = S.build(cfg, n_wg, n_chunks)
+        assert got.dtype == np.int32 and got.shape == want.shape
+        assert np.array_equal(got, want)
+        capi.mkd_schedule_validate(c, got)
+
+
+def test_validator_rejects_mutations():
+    cfg = synth.PRESETS["tiny"]
+    c = capi.make_config(cfg)
+    good = capi.mkd_schedule_build(c, 8, 2)
+    rng = np.random.default_rng(0)
+    body0 = S.WORDS + 8
+    n_bad = 0
+    for trial in range(200):
+        bad = good.copy()
+        k = int(rng.integers(body0, good.size))
+        bad[k] += int(rng.integers(1, 5))
+        try:
+            S.validate(bad, cfg)
+            oracle_ok = True
+        except ValueError:
+            oracle_ok = False
+        try:
+            capi.mkd_schedule_validate(c, bad)
+            lib_ok = True
+        except capi.MkdError:
+            lib_ok = False
+        # a mutation in a padding slot of a short list may be harmless to the
+        # oracle's parse but the library also checks reserved words
+        if not oracle_ok:
+            assert not lib_ok
+        n_bad += not lib_ok
+    assert n_bad > 150

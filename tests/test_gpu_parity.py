@@ -1,0 +1,122 @@
+"""GPU parity: the HIP megakernel (through the C ABI) against the CPU oracle,
+element by element on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import model as om
+from persistent_megakernel_decode_02_amd import capi
+from persistent_megakernel_decode_02_amd.decoder import Decoder
+from persistent_megakernel_decode_02_amd.tuning import launch_config
+from tests.gpu_common import ATOL, RTOL, check_run, close_enough, oracle_run, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(cfg, max_seq, filled, gain_std=0.0):
+    require_gpu()
+    w_gpu = synth.gen_weights(cfg, device="cuda", gain_std=gain_std)
+    kv_gpu = synth.gen_kv_cache(cfg, max_seq, filled, device="cuda")
+    torch.cuda.synchronize()
+    return w_gpu, kv_gpu
+
+
+def test_generator_identical_on_gpu_and_cpu():
+    require_gpu()
+    cfg = synth.PRESETS["tiny"]
+    a = synth.gen_weights(cfg, device="cuda", gain_std=0.1)
+    b = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    for x, y in zip(a, b):
+        assert torch.equal(x.cpu(), y)
+    assert torch.equal(synth.gen_kv_cache(cfg, 40, 33, device="cuda").cpu(), synth.gen_kv_cache(cfg, 40, 33))
+
+
+@pytest.mark.parametrize("n_wg,n_chunks", [(256, 1), (7, 3), (1, 1), (64, 4), (33, 2)])
+def test_tiny_prompt_then_greedy(n_wg, n_chunks):
+    """Tiny config: a 32-token prompt run through the megakernel with forced
+    tokens (the prefill), then 16 greedy steps, in one launch; the oracle does
+    a batched causal prefill and 16 decode steps."""
+    cfg = synth.PRESETS["tiny"]
+    P, N = 32, 16
+    prompt = synth.gen_tokens(P, cfg.vocab)
+    w_gpu, kv_gpu = _setup(cfg, P + N, 0, gain_std=0.1)
+    say(f"tiny n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, P + N, n_wg=n_wg, n_chunks=n_chunks)
+    forced = prompt + [-1] * N
+    toks, logits = dec.decode(prompt[0], 0, P + N, forced=forced)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_after = kv_gpu.cpu()
+    dec.close()
+
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    orc = om.Oracle(cfg, om.Weights.from_list(cfg, w_cpu))
+    kv_o = np.zeros((cfg.n_layers, 2, cfg.n_kv_heads, P + N, cfg.head_dim), dtype=np.float32)
+    pre = orc.prefill(prompt, kv_o)
+    ok, mx, nbad = close_enough(logits[:P], pre)
+    say(f"prefill logits max|err| {mx:.3e}")
+    assert ok, f"prefill logits: {nbad} outside tolerance"
+    # the prompt positions' argmax (tokens_out) must match the oracle's
+    assert [int(x) for x in toks[:P]] == [int(np.argmax(r)) for r in pre]
+    otoks, ologits = orc.decode(int(np.argmax(pre[-1])), P, N, kv_o)
+    # GPU step P consumes argmax of step P-1 (= the prefill's last row)
+    check_run("tiny decode", toks[P:], logits[P:], otoks, ologits)
+    # the cache the kernel appended: every position, K and V, all layers
+    kv_g = kv_after.float().numpy()
+    ok, mx, nbad = close_enough(kv_g, kv_o)
+    say(f"kv cache max|err| {mx:.3e}")
+    assert ok, f"kv cache: {nbad} values outside tolerance"
+
+
+def test_tiny_kv_context_and_determinism():
+    """Tiny config from a random-filled cache (the long-context recipe at
+    small size); two launches from the same state are bit-identical and the
+    pre-filled positions are left untouched."""
+    cfg = synth.PRESETS["tiny"]
+    T0, N = 200, 9
+    w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
+    kv0 = kv_gpu.clone()
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=64, n_chunks=5)
+    first = synth.gen_tokens(1, cfg.vocab, stream=7)[0]
+    t1, l1 = dec.decode(first, T0, N)
+    t2, l2 = dec.decode(first, T0, N)
+    assert torch.equal(t1, t2) and torch.equal(l1, l2), "two identical launches differ"
+    assert torch.equal(kv_gpu[:, :, :, :T0], kv0[:, :, :, :T0])
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    otoks, ologits, kv_o = oracle_run(cfg, w_cpu, synth.gen_kv_cache(cfg, T0 + N, T0), first, T0, N)
+    check_run("tiny ctx", t1.cpu().numpy(), l1.cpu().numpy(), otoks, ologits)
+    ok, mx, _ = close_enough(kv_gpu.cpu().float().numpy(), kv_o)
+    assert ok, f"kv cache max err {mx}"
+
+
+def _full_size(name, T0, N, n_wg=None, n_chunks=None):
+    cfg = synth.PRESETS[name]
+    max_seq = T0 + N
+    w_gpu, kv_gpu = _setup(cfg, max_seq, T0)
+    nw, nc = launch_config(cfg, T0, N)
+    n_wg = n_wg or nw
+    n_chunks = n_chunks or nc
+    say(f"{name} T0={T0} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, max_seq, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    del w_gpu, kv_gpu
+    torch.cuda.empty_cache()
+    say("generating oracle inputs on the host")
+    w_cpu = synth.gen_weights(cfg, device="cpu")
+    kv_cpu = synth.gen_kv_cache(cfg, max_seq, T0)
+    otoks, ologits, kv_o = oracle_run(cfg, w_cpu, kv_cpu, first, T0, N)
+    check_run(f"{name}@{T0}", toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"
+
+
+def test_llama1b_full_size_kv128():
+    _full_size("llama1b", 128, 6)
+
+
+def test_llama1b_full_size_kv1024_split():
+    _full_size("llama1b", 1024, 3)
