@@ -110,9 +110,10 @@ int mkd_weight_shape(const mkd_config* cfg, size_t index, int64_t* rows, int64_t
  * bf16 [n_layers][2 (K, V)][n_kv_heads][max_seq][head_dim]. */
 int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out);
 
-/* Build the instruction tensor (schedule spec v1) on the host, without a
+/* Build the instruction tensor (schedule spec v2) on the host, without a
  * device.  The spec -- stage order, GEMV row tiling, round-robin block
- * assignment, word layout -- is this library's own; the pages fix none of it
+ * assignment (O-projection tiles skip the blocks that ran attention or its
+ * reduction), word layout -- is this library's own; the pages fix none of it
  * (they only say the blocks follow a host-built schedule of every operation,
  * Hyperkernel teardown, "What a megakernel buys").
  * n_wg >= 1 workgroups, n_chunks >= 1 split-KV chunks per KV head.
@@ -188,13 +189,20 @@ int mkd_abort(mkd_model* m);
  * on another's output (default 2000).  Must be >= 1. */
 int mkd_set_watchdog(mkd_model* m, int32_t watchdog_ms);
 
-/* Per-instruction timestamps: when trace_dev is non-NULL, each launch writes
- * trace_dev[((wg * n_steps + step) * max_instr + i) * 2 + {0,1}] = wall-clock
- * ticks at the start and end of instruction i of workgroup wg at each step
- * (ticks at mkd_device_info's clock; unused slots untouched).  capacity_words
- * must cover n_wg * n_steps * max_instr * 2 at each mkd_decode, else
- * MKD_E_INVALID.  NULL turns tracing off. */
+/* Per-instruction timestamps: when trace_dev is non-NULL, each launch writes,
+ * for instruction i of workgroup wg at decode step `step`, four words at
+ * trace_dev[((wg * n_steps + step) * max_instr + i) * 4]: wall-clock ticks
+ * when the instruction starts, when its inputs are ready, and when it has
+ * published its outputs (the fourth word is unused); ticks at mkd_clock_hz.
+ * capacity_words must cover n_wg * n_steps * max_instr * 4 at each
+ * mkd_decode, else MKD_E_INVALID.  NULL turns tracing off. */
 int mkd_set_trace(mkd_model* m, uint64_t* trace_dev, size_t capacity_words);
+
+/* Duration in milliseconds of the last launch's megakernel alone, from HIP
+ * events recorded on its stream just before and after the cooperative kernel
+ * (the small buffer-reset kernel that precedes it is outside the interval).
+ * Call after mkd_wait.  MKD_E_INVALID if nothing has run. */
+int mkd_kernel_ms(mkd_model* m, float* ms);
 
 /* Wall-clock tick rate of the device in Hz (for trace and watchdog). */
 int mkd_clock_hz(mkd_model* m, double* hz);

@@ -6,10 +6,10 @@ each block reads a host-built instruction tensor to decide its next work
 in the forward pass" and synchronise on the device (Hyperkernel teardown,
 "What a megakernel buys").  The pages fix no format, tiling or assignment, so
 the tensor below is this project's own specification ("schedule spec v1",
-written out in the design notes); the GPU library's C++ builder must produce
+written out in the design notes, "schedule spec v2"); the GPU library's C++ builder must produce
 the same bytes.
 
-Spec v1 (all int32):
+Spec v2 (all int32):
 
 * stage order per token: for each layer ``QKV, ATTN, [AREDUCE if n_chunks > 1],
   OPROJ, UPGATE|MOE_UPGATE, DOWN|MOE_DOWN``; then ``LMHEAD``.
@@ -18,8 +18,13 @@ Spec v1 (all int32):
   UPGATE = F, MOE_UPGATE = top_k * F, LMHEAD = V.
 * ATTN has ``hkv * n_chunks`` instructions (kv_head = i // n_chunks,
   chunk = i % n_chunks); AREDUCE has hq (q_head = i).
-* instruction i of a stage goes to block ``i % n_wg``; a block's list is the
-  concatenation of its instructions in stage order.
+* instruction i of a stage goes to block ``(offset + i) % n_wg``; a block's
+  list is the concatenation of its instructions in stage order.  The offset
+  is 0 except for OPROJ: its tiles skip the blocks that ran the stage just
+  before it (ATTN, or AREDUCE when n_chunks > 1), whose O-projection would
+  otherwise start late and hold up the whole stage -- when there are more
+  blocks than that, OPROJ has ``min(d, n_wg - E)`` tiles at offset E, E being
+  the preceding stage's instruction count.
 * words: header[16] = {magic, version, n_wg, n_stages, max_instr, n_chunks, L,
   d, hq, hkv, hd, F, V, E, top_k, total_instr}; counts[n_wg]; then
   ``[n_wg][max_instr][16]`` with instruction = {opcode, layer, stage, index,
@@ -42,7 +47,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 MAGIC = 0x314B444D
-VERSION = 1
+VERSION = 2
 WORDS = 16
 
 OP_QKV, OP_ATTN, OP_AREDUCE, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD = range(1, 10)
@@ -72,8 +77,19 @@ def stages(cfg, n_chunks: int) -> List[Tuple[int, int, int]]:
     return out
 
 
+def placement(st: List[Tuple[int, int, int]], s: int, n_wg: int) -> Tuple[int, int]:
+    """(blocks available, first block) for stage s."""
+    op = st[s][0]
+    if op == OP_OPROJ:
+        prev_count = st[s - 1][2]          # ATTN or AREDUCE instruction count
+        if n_wg > prev_count:
+            return n_wg - prev_count, prev_count
+    return n_wg, 0
+
+
 def stage_instructions(op: int, layer: int, size: int, n_wg: int, n_chunks: int) -> List[Tuple[int, int]]:
-    """The (a, b) operand pairs of one stage's instructions, by index."""
+    """The (a, b) operand pairs of one stage's instructions, by index;
+    ``n_wg`` is the number of blocks the stage may use."""
     if op in GEMV_OPS:
         n = min(n_wg, size)
         return [(i * size // n, (i + 1) * size // n) for i in range(n)]
@@ -91,16 +107,19 @@ def build(cfg, n_wg: int, n_chunks: int) -> np.ndarray:
     st = stages(cfg, n_chunks)
     n_st = len(st)
     lists: List[List[List[int]]] = [[] for _ in range(n_wg)]
-    counts_per_stage = [len(stage_instructions(op, l, sz, n_wg, n_chunks)) for op, l, sz in st]
+    places = [placement(st, s, n_wg) for s in range(n_st)]
+    counts_per_stage = [len(stage_instructions(op, l, sz, places[s][0], n_chunks))
+                        for s, (op, l, sz) in enumerate(st)]
     for s, (op, l, sz) in enumerate(st):
         if s == 0:
             wait_stage, wait_prev = n_st - 1, 1
         else:
             wait_stage, wait_prev = s - 1, 0
-        for i, (a, b) in enumerate(stage_instructions(op, l, sz, n_wg, n_chunks)):
+        avail, first = places[s]
+        for i, (a, b) in enumerate(stage_instructions(op, l, sz, avail, n_chunks)):
             words = [op, l, s, i, a, b, wait_stage, counts_per_stage[wait_stage], wait_prev, s]
             words += [0] * (WORDS - len(words))
-            lists[i % n_wg].append(words)
+            lists[(first + i) % n_wg].append(words)
     max_instr = max(len(x) for x in lists)
     total = sum(len(x) for x in lists)
     hdr = [MAGIC, VERSION, n_wg, n_st, max_instr, n_chunks, cfg.n_layers, cfg.d_model,
@@ -143,7 +162,8 @@ def validate(words: np.ndarray, cfg) -> None:
             if s < prev:
                 raise ValueError(f"wg {w}: list not in stage order")
             prev = s
-            if i % n_wg != w:
+            avail, first = placement(st, s, n_wg)
+            if (first + i) % n_wg != w:
                 raise ValueError(f"wg {w}: instruction {i} of stage {s} on the wrong block")
             if sig != s:
                 raise ValueError("signal stage")
@@ -153,7 +173,7 @@ def validate(words: np.ndarray, cfg) -> None:
             seen[s].append((i, a, b))
     for s, (op, l, sz) in enumerate(st):
         got = sorted(seen[s])
-        want = stage_instructions(op, l, sz, n_wg, n_chunks)
+        want = stage_instructions(op, l, sz, placement(st, s, n_wg)[0], n_chunks)
         if [x[0] for x in got] != list(range(len(want))):
             raise ValueError(f"stage {s}: instruction indices")
         if [(x[1], x[2]) for x in got] != want:

@@ -27,12 +27,16 @@ ERROR_NAMES = {0: "MKD_OK", -1: "MKD_E_INVALID", -2: "MKD_E_HIP", -3: "MKD_E_COO
                -4: "MKD_E_TIMEOUT", -5: "MKD_E_WATCHDOG", -6: "MKD_E_BOUNDS",
                -7: "MKD_E_NONFINITE", -8: "MKD_E_ABORTED", -9: "MKD_E_UNSUPPORTED"}
 
+# instruction opcodes of the schedule tensor (csrc/mkd_internal.h)
+OPCODE_NAMES = {1: "QKV", 2: "ATTN", 3: "AREDUCE", 4: "OPROJ", 5: "UPGATE", 6: "DOWN",
+                7: "MOE_UPGATE", 8: "MOE_DOWN", 9: "LMHEAD"}
+
 # every function include/mkd.h declares
 EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_count",
            "mkd_weight_shape", "mkd_kv_cache_bytes", "mkd_schedule_build",
            "mkd_schedule_validate", "mkd_init", "mkd_device_info", "mkd_build_schedule",
            "mkd_load_schedule", "mkd_decode", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
-           "mkd_set_trace", "mkd_clock_hz", "mkd_destroy")
+           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_destroy")
 
 
 class mkd_config(ctypes.Structure):
@@ -88,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "mkd_abort": ([P], ctypes.c_int),
         "mkd_set_watchdog": ([P, I32], ctypes.c_int),
         "mkd_set_trace": ([P, P, SZ], ctypes.c_int),
+        "mkd_kernel_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mkd_clock_hz": ([P, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "mkd_destroy": ([P], None),
     }
@@ -225,6 +230,12 @@ def mkd_set_watchdog(m: int, watchdog_ms: int) -> None:
 
 def mkd_set_trace(m: int, trace=None) -> None:
     _check(load().mkd_set_trace(m, _ptr(trace), 0 if trace is None else trace.numel()))
+
+
+def mkd_kernel_ms(m: int) -> float:
+    ms = ctypes.c_float()
+    _check(load().mkd_kernel_ms(m, ctypes.byref(ms)))
+    return ms.value
 
 
 def mkd_clock_hz(m: int) -> float:

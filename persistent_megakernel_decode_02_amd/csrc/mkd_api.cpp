@@ -8,6 +8,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <chrono>
 #include <string>
 #include <thread>
@@ -44,17 +45,20 @@ struct mkd_model {
   uint64_t* d_wtab = nullptr;
   float* d_rope = nullptr;
   int32_t* d_status = nullptr;
+  void* d_zero = nullptr;   // 4 KiB of zeros: streamer loads past the end of a tile
   int32_t* h_stop = nullptr;
   uint64_t* d_ll = nullptr;
   size_t ll_words = 0, ll_cap = 0;
   // sub-buffers of d_ll
   uint64_t *h = nullptr, *qkv = nullptr, *part = nullptr, *aout = nullptr, *hmid = nullptr,
-           *act = nullptr, *route = nullptr, *lm = nullptr;
+           *act = nullptr, *route = nullptr, *lm = nullptr, *flags = nullptr;
   int32_t* d_sched = nullptr;
   size_t sched_words = 0, sched_cap = 0;
-  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0;
+  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, n_stages = 0;
+  int flag_stride = 0;
   hipEvent_t done = nullptr;
-  bool launched = false;
+  hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
+  bool launched = false, timed = false;
   double clock_hz = 100e6;
   uint64_t watchdog_ticks = 0;
   uint64_t* trace = nullptr;
@@ -206,6 +210,8 @@ int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights
   if ((e = hipMalloc(&m->d_wtab, m->wptr.size() * 8)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc wtab");
   if ((e = hipMalloc(&m->d_rope, rope.size() * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc rope");
   if ((e = hipMalloc(&m->d_status, S_WORDS * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc status");
+  if ((e = hipMalloc(&m->d_zero, 4096)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc zero");
+  if ((e = hipMemset(m->d_zero, 0, 4096)) != hipSuccess) return cleanup(MKD_E_HIP, "clear zero");
   if ((e = hipHostMalloc(&m->h_stop, 64, hipHostMallocDefault)) != hipSuccess)
     return cleanup(MKD_E_HIP, "hipHostMalloc stop word");
   memset(m->h_stop, 0, 64);
@@ -215,6 +221,8 @@ int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights
     return cleanup(MKD_E_HIP, "upload rope");
   if ((e = hipMemset(m->d_status, 0, S_WORDS * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "clear status");
   if ((e = hipEventCreateWithFlags(&m->done, hipEventDisableTiming)) != hipSuccess)
+    return cleanup(MKD_E_HIP, "hipEventCreate");
+  if ((e = hipEventCreate(&m->k0)) != hipSuccess || (e = hipEventCreate(&m->k1)) != hipSuccess)
     return cleanup(MKD_E_HIP, "hipEventCreate");
   *out = m;
   return MKD_OK;
@@ -228,9 +236,12 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
   int got = 0;
   stage_list(c, n_chunks, st.data(), &got, n_st);
   int best = 4;
-  for (const StageDesc& s : st) {
+  for (int i = 0; i < n_st; ++i) {
+    const StageDesc& s = st[i];
     if (!is_gemv(s.op)) continue;
-    const int n = s.size < n_wg ? s.size : n_wg;
+    int avail = n_wg, first = 0;
+    placement(st, i, n_wg, &avail, &first);
+    const int n = s.size < avail ? s.size : avail;
     int rows = (s.size + n - 1) / n;
     if (s.op == OP_UPGATE || s.op == OP_MOE_UPGATE || s.op == OP_MOE_DOWN) rows *= 2;
     best = rows > best ? rows : best;
@@ -241,9 +252,10 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
 static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm) {
   const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
   const int qd = c->n_q_heads * hd;
-  int x = c->d_model;
-  x = x > qd ? x : qd;
-  const int act = c->d_ff * (c->top_k ? c->top_k : 1);
+  auto pad = [](int n) { return (n + 511) & ~511; };   // streamer rows read x in 512-wide segments
+  int x = pad(c->d_model);
+  x = x > pad(qd) ? x : pad(qd);
+  const int act = pad(c->d_ff) * (c->top_k ? c->top_k : 1);
   x = x > act ? x : act;
   x = x > 2 * n_lm ? x : 2 * n_lm;
   const int ared = n_chunks * (hd + 2);
@@ -306,12 +318,26 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   if ((e = hipMemcpy(m->d_sched, words, n * 4, hipMemcpyHostToDevice)) != hipSuccess)
     return hip_fail(e, "upload schedule");
   m->sched_words = n;
+  // completion flags: one word per instruction of each stage
+  int flag_stride = kFlagAlign;
+  {
+    const int n_st = words[H_NSTAGES];
+    std::vector<int> per(n_st, 0);
+    const int32_t* body = words + kWords + n_wg;
+    for (int w = 0; w < n_wg; ++w)
+      for (int j = 0; j < words[kWords + w]; ++j) {
+        const int32_t* ins = body + ((size_t)w * words[H_MAXINSTR] + j) * kWords;
+        per[ins[I_STAGE]] = std::max(per[ins[I_STAGE]], ins[I_INDEX] + 1);
+      }
+    for (int v : per) flag_stride = std::max(flag_stride, (v + kFlagAlign - 1) / kFlagAlign * kFlagAlign);
+  }
   // tagged activation buffers, one allocation (cleared before each launch)
   const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
-  const size_t sz[8] = {round16(c->d_model), round16(qd + 2 * kvd),
+  const size_t sz[9] = {round16(c->d_model), round16(qd + 2 * kvd),
                         round16((size_t)c->n_q_heads * n_chunks * (c->head_dim + 2)), round16(qd),
                         round16(c->d_model), round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1)),
-                        16, round16(2 * (size_t)n_lm)};
+                        16, round16(2 * (size_t)n_lm),
+                        round16((size_t)words[H_NSTAGES] * flag_stride / 2)};
   size_t total = 0;
   for (size_t s : sz) total += s;
   if (total > m->ll_cap) {
@@ -323,8 +349,10 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   }
   m->ll_words = total;
   uint64_t* q = m->d_ll;
-  uint64_t** dst[8] = {&m->h, &m->qkv, &m->part, &m->aout, &m->hmid, &m->act, &m->route, &m->lm};
-  for (int i = 0; i < 8; ++i) { *dst[i] = q; q += sz[i]; }
+  uint64_t** dst[9] = {&m->h, &m->qkv, &m->part, &m->aout, &m->hmid, &m->act, &m->route, &m->lm, &m->flags};
+  for (int i = 0; i < 9; ++i) { *dst[i] = q; q += sz[i]; }
+  m->n_stages = words[H_NSTAGES];
+  m->flag_stride = flag_stride;
   m->n_wg = n_wg;
   m->n_chunks = n_chunks;
   m->max_instr = words[H_MAXINSTR];
@@ -375,7 +403,7 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   if (start_pos < 0 || n_steps < 1 || (int64_t)start_pos + n_steps > m->max_seq)
     return fail(MKD_E_INVALID, "need start_pos >= 0, n_steps >= 1, start_pos + n_steps <= max_seq");
   if (!tokens_out_dev) return fail(MKD_E_INVALID, "null tokens_out_dev");
-  if (m->trace && m->trace_cap < (size_t)m->n_wg * n_steps * m->max_instr * 2)
+  if (m->trace && m->trace_cap < (size_t)m->n_wg * n_steps * m->max_instr * kTraceWords)
     return fail(MKD_E_INVALID, "trace buffer too small for this launch");
   if ((int64_t)n_steps * (c->n_layers + 1) >= 0xffffffffll) return fail(MKD_E_INVALID, "n_steps too large");
   hipError_t e = hipSetDevice(m->device);
@@ -387,6 +415,10 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   p.rope = m->d_rope;
   p.h = m->h; p.qkv = m->qkv; p.part = m->part; p.aout = m->aout;
   p.hmid = m->hmid; p.act = m->act; p.route = m->route; p.lm = m->lm;
+  p.flags = (uint32_t*)m->flags;
+  p.flag_stride = m->flag_stride;
+  p.zero = m->d_zero;
+  p.n_stages = m->n_stages;
   p.forced = forced_dev;
   p.tokens_out = tokens_out_dev;
   p.logits_out = logits_out_dev;
@@ -404,8 +436,9 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   p.out_floats = m->out_floats;
   p.eps = c->rms_eps;
   const char* why = "";
-  const int rc = launch(p, m->ll_words, stream, &why);
+  const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, &why);
   if (rc) return fail(rc, why);
+  m->timed = true;
   if ((e = hipEventRecord(m->done, (hipStream_t)stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   m->launched = true;
   return MKD_OK;
@@ -460,6 +493,15 @@ int mkd_set_trace(mkd_model* m, uint64_t* trace_dev, size_t capacity_words) {
   return MKD_OK;
 }
 
+int mkd_kernel_ms(mkd_model* m, float* ms) {
+  if (!m || !ms) return fail(MKD_E_INVALID, "null argument");
+  if (!m->timed) return fail(MKD_E_INVALID, "no launch has been timed");
+  hipSetDevice(m->device);
+  const hipError_t e = hipEventElapsedTime(ms, m->k0, m->k1);
+  if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  return MKD_OK;
+}
+
 int mkd_clock_hz(mkd_model* m, double* hz) {
   if (!m || !hz) return fail(MKD_E_INVALID, "null argument");
   *hz = m->clock_hz;
@@ -471,9 +513,12 @@ void mkd_destroy(mkd_model* m) {
   hipSetDevice(m->device);
   if (m->launched && m->done) hipEventSynchronize(m->done);
   if (m->done) hipEventDestroy(m->done);
+  if (m->k0) hipEventDestroy(m->k0);
+  if (m->k1) hipEventDestroy(m->k1);
   if (m->d_wtab) hipFree(m->d_wtab);
   if (m->d_rope) hipFree(m->d_rope);
   if (m->d_status) hipFree(m->d_status);
+  if (m->d_zero) hipFree(m->d_zero);
   if (m->h_stop) hipHostFree(m->h_stop);
   if (m->d_ll) hipFree(m->d_ll);
   if (m->d_sched) hipFree(m->d_sched);

@@ -4,13 +4,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "mkd.h"
 
 namespace mkd {
 
-// ---------------------------------------------------------------- schedule spec v1
+// ---------------------------------------------------------------- schedule spec v2
 constexpr int32_t kMagic = 0x314B444D;
-constexpr int32_t kVersion = 1;
+constexpr int32_t kVersion = 2;
 constexpr int kWords = 16;  // words per header and per instruction
 
 enum Opcode : int32_t {
@@ -41,6 +43,8 @@ struct StageDesc {
 int config_check(const mkd_config* c, const char** why);
 void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, int cap);
 int stage_count(const mkd_config* c, int n_chunks);
+// blocks stage s may use, and the first of them (spec v2 placement)
+void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, int* first);
 bool is_gemv(int op);
 int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, size_t cap,
                    size_t* n_words, const char** why);
@@ -49,6 +53,8 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
 // ---------------------------------------------------------------- device parameters
 constexpr int kThreads = 512;  // 8 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
+constexpr int kFlagAlign = 64;   // per-stage flag arrays start on 256-byte boundaries
+constexpr int kTraceWords = 4;   // per instruction: start, inputs ready, end, unused
 
 // weight pointer table layout: global slots, then per-layer slots
 constexpr int W_EMBED = 0, W_FINAL_NORM = 1, W_LM_HEAD = 2, W_GLOBAL = 3;
@@ -74,6 +80,8 @@ struct KParams {
   uint64_t* act;             // [top_k * F] (or F)
   uint64_t* route;           // [4]   (expert a, expert b, weight a, weight b)
   uint64_t* lm;              // [2 * n_lm_tiles] (tile max, tile argmax)
+  uint32_t* flags;           // [n_stages][flag_stride]: step + 1 once instruction i of a stage is done
+  const void* zero;          // >= 1 KiB of readable memory (streamer slots past the end)
   const int32_t* forced;     // [n_steps] or null
   int32_t* tokens_out;       // [n_steps]
   float* logits_out;         // [n_steps][V] or null
@@ -81,7 +89,7 @@ struct KParams {
   const int32_t* stop;       // pinned host word
   uint64_t* trace;           // or null
   uint64_t watchdog_ticks;
-  int32_t n_wg, max_instr, n_chunks, n_lm_tiles;
+  int32_t n_wg, max_instr, n_chunks, n_lm_tiles, n_stages, flag_stride;
   int32_t first_token, start_pos, n_steps, max_seq;
   int32_t L, d, hq, hkv, hd, F, V, E, topk, qd, kvd, G, tied, lslots;
   int32_t x_floats;          // LDS floats reserved for the staged input vector
@@ -91,7 +99,8 @@ struct KParams {
 
 size_t lds_bytes(const KParams& p);
 // launch the reset kernel and the cooperative megakernel on `stream`
-int launch(const KParams& p, size_t ll_words, void* stream, const char** why);
+// ev0/ev1 (may be null) are recorded around the cooperative kernel alone
+int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why);
 int max_coop_blocks(int device, size_t lds, int* out);
 
 }  // namespace mkd

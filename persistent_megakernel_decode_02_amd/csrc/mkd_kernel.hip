@@ -48,6 +48,19 @@ __device__ __forceinline__ uint16_t ld_u16(const void* p) { return *(GLOBAL cons
 __device__ __forceinline__ float ld_f32(const void* p) { return *(GLOBAL const float*)p; }
 __device__ __forceinline__ int ld_i32(const void* p) { return *(GLOBAL const int*)p; }
 __device__ __forceinline__ uint64_t ld_u64(const void* p) { return *(GLOBAL const uint64_t*)p; }
+// Tables that stay constant for a whole launch (weight pointers, the
+// instruction tensor) are read through the constant address space: uniform
+// addresses then become scalar loads and the values live in scalar registers.
+#define CONSTANT __attribute__((address_space(4)))
+__device__ __forceinline__ uint64_t ldc_u64(const void* p) { return *(CONSTANT const uint64_t*)p; }
+__device__ __forceinline__ int ldc_i32(const void* p) { return *(CONSTANT const int*)p; }
+
+// The launch parameters, read in place from the kernel-argument segment.
+// Keeping the constant address space on every access matters: a load
+// through a generic pointer counts as divergent (generic addresses may be
+// per-lane scratch), which would move every pointer and loop bound derived
+// from the parameters into vector registers.
+typedef CONSTANT const KParams CKParams;
 __device__ __forceinline__ void st_f32(float* p, float v) { *(GLOBAL float*)p = v; }
 __device__ __forceinline__ void st_i32(int32_t* p, int32_t v) { *(GLOBAL int32_t*)p = v; }
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { *(GLOBAL uint64_t*)p = v; }
@@ -57,6 +70,7 @@ constexpr int ARING = 4;      // K/V position steps in flight per lane (attentio
 constexpr int kRed = 256;     // LDS floats reserved for reductions
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kSC1 = 16;                     // cache-policy bit: device-coherent access
+constexpr int kNT = 2;                       // cache-policy bit: non-temporal (streamed once)
 
 // ---------------------------------------------------------------- small helpers
 
@@ -115,27 +129,29 @@ __device__ __forceinline__ const uint16_t* psel(bool b, const uint16_t* x, const
   return (const uint16_t*)(((uint64_t)x & ~m) | ((uint64_t)y & m));
 }
 
-__device__ __forceinline__ uint32_t tag_of(const KParams& p, int t, int l) {
+__device__ __forceinline__ uint32_t tag_of(CKParams& p, int t, int l) {
   return 1u + (uint32_t)t * (uint32_t)(p.L + 1) + (uint32_t)l;
 }
 
-__device__ __forceinline__ const uint16_t* wptr(const KParams& p, int slot) {
-  return (const uint16_t*)ld_u64(p.wtab + slot);
+__device__ __forceinline__ const uint16_t* wptr(CKParams& p, int slot) {
+  return (const uint16_t*)ldc_u64(p.wtab + slot);
 }
-__device__ __forceinline__ const uint16_t* lptr(const KParams& p, int layer, int slot) {
-  return (const uint16_t*)ld_u64(p.wtab + W_GLOBAL + layer * p.lslots + slot);
+__device__ __forceinline__ const uint16_t* lptr(CKParams& p, int layer, int slot) {
+  return (const uint16_t*)ldc_u64(p.wtab + W_GLOBAL + layer * p.lslots + slot);
 }
 
 // ---------------------------------------------------------------- per-workgroup context
 
 struct Ctx {
-  const KParams& p;
+  CKParams& p;
   float* xs;     // staged input vector   [x_floats]
   float* res;    // residual rows         [d]
   float* out;    // GEMV row results      [out_floats]
   float* red;    // reduction scratch     [kRed]
   volatile int* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
   int wg, instr, t, tid, lane, wave;
+  int stage, index, wait_stage, wait_count, wait_prev;  // from the instruction words
+  uint64_t* tr;                                  // this instruction's trace entry, or null
 };
 
 // Record a device error: the first raiser records where; with stop_all every
@@ -216,10 +232,85 @@ __device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uin
 }
 
 // workgroup barrier; false when the launch is being aborted
+// (values read from LDS after a barrier are the same in every lane; reading
+// them through readfirstlane tells the compiler so, which keeps the control
+// flow that depends on them uniform and its loop counters in scalar registers)
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ bool sync_ok(Ctx& c) {
   __syncthreads();
-  const bool ok = c.sflag[0] == 0;
-  return ok;
+  return uni(c.sflag[0]) == 0;
+}
+
+// Wait until all `count` instructions of `stage` have published step
+// `step_plus1 - 1` (their completion flags hold step + 1).  Wavefront 0 reads
+// the stage's flags -- one word per producer, so a single wide load covers
+// 256 producers -- and repeats with a short sleep until every flag is there.
+// Producers only store their own flag (no read-modify-write on a shared
+// word, which would serialise 256 workgroups at one address).  False when
+// the launch is being aborted.
+__device__ __forceinline__ bool wait_counter(Ctx& c, int stage, uint32_t step_plus1, int count) {
+  CKParams& p = c.p;
+  if (c.wave == 0 && step_plus1 > 0) {
+    const uint32_t* f = p.flags + (size_t)stage * p.flag_stride;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(f, (uint32_t)count * 4u);
+    const uint64_t t0 = wall_clock64();
+    for (int it = 0;; ++it) {
+      bool mine = true;
+      for (int base = 0; base < count; base += 256) {
+        const int j = base + c.lane * 4;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, c.lane * 16, base * 4, kSC1);
+        mine = mine && (j + 0 >= count || v.x >= step_plus1) && (j + 1 >= count || v.y >= step_plus1) &&
+               (j + 2 >= count || v.z >= step_plus1) && (j + 3 >= count || v.w >= step_plus1);
+      }
+      if (__builtin_amdgcn_ballot_w64(!mine) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+      if ((it & 31) == 31) {
+        int stop = 0;
+        if (__hip_atomic_load(&p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          stop = 1;
+        } else if (__hip_atomic_load(p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+          stop = 2;
+        } else if (wall_clock64() - t0 > p.watchdog_ticks) {
+          stop = 3;
+        }
+        stop = uni(stop);
+        if (stop) {
+          if (c.lane == 0) {
+            if (stop == 1) c.sflag[0] = 1;
+            else raise_error(c, stop == 2 ? MKD_E_ABORTED : MKD_E_WATCHDOG, true);
+          }
+          break;
+        }
+      }
+    }
+  }
+  return sync_ok(c);
+}
+
+// the wait this instruction's schedule words name
+__device__ __forceinline__ bool wait_inputs(Ctx& c) {
+  return wait_counter(c, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count);
+}
+
+// Mark this instruction done for this step.  Called after every thread has
+// issued its output stores; the flag may become visible before those stores
+// do, which is harmless: consumers still check each word's tag.
+__device__ __forceinline__ void signal_done(Ctx& c) {
+  __syncthreads();
+  if (c.tid == 0) {
+    __hip_atomic_store(c.p.flags + (size_t)c.stage * c.p.flag_stride + c.index, (uint32_t)(c.t + 1),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c.tr) st_u64(c.tr + 2, wall_clock64());
+  }
+}
+
+__device__ __forceinline__ void mark_ready(Ctx& c) {
+  if (c.tr && c.tid == 0) st_u64(c.tr + 1, wall_clock64());
+}
+
+__device__ __forceinline__ void mark_computed(Ctx& c) {
+  if (c.tr && c.tid == 0) st_u64(c.tr + 3, wall_clock64());
 }
 
 // sum of v over the workgroup (all threads call; result in all threads)
@@ -234,13 +325,63 @@ __device__ __forceinline__ float block_sum(Ctx& c, float v) {
   return s;
 }
 
-// xs[0..d) <- rmsnorm(xs) * gamma  (fp32; gamma bf16)
-__device__ __forceinline__ void rmsnorm_lds(Ctx& c, int d, const uint16_t* gamma) {
+// One tagged input vector: n words at src, expected tag, LDS destination.
+struct Fetch {
+  const uint64_t* src;
+  int n;
+  uint32_t tag;
+  float* dst;
+};
+
+// Stage an instruction's inputs: wait on the producing stage's counter (one
+// word, polled by one thread), then read every word once, spinning per word
+// on any whose store is still in flight.  Reading the vectors before the
+// counter completes would mostly read them twice: in this schedule a
+// workgroup nearly always reaches a stage before its producers finish.
+template <int K>
+__device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count) {
+  if (!wait_counter(c, stage, step_plus1, count)) return false;
+#pragma unroll
+  for (int j = 0; j < K; ++j) ll_fetch(c, f[j].src, f[j].n, f[j].tag, f[j].dst);
+  if (!sync_ok(c)) return false;
+  mark_ready(c);
+  return true;
+}
+
+template <int K>
+__device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K]) {
+  return gather<K>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count);
+}
+
+// RMSNorm gains of this thread's elements (i = tid + k * kThreads), read
+// before the inputs are waited for; covers d <= kGainRegs * kThreads
+constexpr int kGainRegs = 8;
+struct Gains {
+  float g[kGainRegs];
+};
+__device__ __forceinline__ Gains load_gains(Ctx& c, int d, const uint16_t* gamma) {
+  Gains r;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = c.tid + k * kThreads;
+    r.g[k] = bf_val(ld_u16(gamma + (i < d ? i : d - 1)));
+  }
+  return r;
+}
+
+// xs[0..d) <- rmsnorm(xs) * gamma  (fp32)
+__device__ __forceinline__ void rmsnorm_g(Ctx& c, int d, const uint16_t* gamma, const Gains& gr) {
   float ss = 0.f;
   for (int i = c.tid; i < d; i += kThreads) ss = fmaf(c.xs[i], c.xs[i], ss);
   const float tot = block_sum(c, ss);
   const float inv = 1.0f / sqrtf(tot / (float)d + c.p.eps);
-  for (int i = c.tid; i < d; i += kThreads) c.xs[i] = (c.xs[i] * inv) * bf_val(ld_u16(gamma + i));
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = c.tid + k * kThreads;
+    if (i < d) c.xs[i] = (c.xs[i] * inv) * gr.g[k];
+  }
+  for (int i = c.tid + kGainRegs * kThreads; i < d; i += kThreads)
+    c.xs[i] = (c.xs[i] * inv) * bf_val(ld_u16(gamma + i));
   __syncthreads();
 }
 
@@ -253,10 +394,12 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 
 // argmax of step tt's logits from the LM-head tile partials
 __device__ __forceinline__ int fold_argmax(Ctx& c, int tt, bool* ok) {
-  const KParams& p = c.p;
-  const int n = 2 * p.n_lm_tiles;
-  ll_fetch(c, p.lm, n, tag_of(p, tt, p.L), c.xs);
-  if (!sync_ok(c)) { *ok = false; return 0; }
+  CKParams& p = c.p;
+  const Fetch f[1] = {{p.lm, 2 * p.n_lm_tiles, tag_of(p, tt, p.L), c.xs}};
+  if (!gather<1>(c, f, p.n_stages - 1, (uint32_t)(tt + 1), p.n_lm_tiles)) {
+    *ok = false;
+    return 0;
+  }
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for (int k = c.tid; k < p.n_lm_tiles; k += kThreads) {
@@ -279,19 +422,19 @@ __device__ __forceinline__ int fold_argmax(Ctx& c, int tt, bool* ok) {
     if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
   __syncthreads();
   *ok = true;
-  return bi;
+  return uni(bi);
 }
 
 // token consumed at step t (cached per step in LDS)
 __device__ __forceinline__ int step_token(Ctx& c, bool* ok) {
-  const KParams& p = c.p;
+  CKParams& p = c.p;
   *ok = true;
-  if (c.sflag[2] == c.t) return c.sflag[1];
+  if (uni(c.sflag[2]) == c.t) return uni(c.sflag[1]);
   int tok;
   if (c.t == 0) {
     tok = p.first_token;
   } else {
-    const int f = p.forced ? ld_i32(p.forced + c.t) : -1;
+    const int f = p.forced ? uni(ld_i32(p.forced + c.t)) : -1;
     int am = 0;
     if (f < 0 || c.wg == 0) {
       am = fold_argmax(c, c.t - 1, ok);
@@ -324,28 +467,34 @@ __device__ __forceinline__ int step_token(Ctx& c, bool* ok) {
 template <class Map>
 struct RowStream {
   const Map& m;
-  const int K, nseg, S, lane;
-  int pk, pseg, ps;
-  const u32x4* prow;
-  const u32x4* dummy;
+  const int K, nseg, S;
+  const uint32_t lane16;   // this lane's byte offset inside a 1 KiB segment
+  const int lane;
+  int ps, pseg, pk;        // producer cursor (wave-uniform)
+  const char* row;         // the producer's current row
   u32x4 ring[RING];
 
-  __device__ __forceinline__ RowStream(const Map& m_, int K_, int nrows, int lane_, const void* dummy_)
-      : m(m_), K(K_), nseg((K_ + 511) >> 9), S(nrows * ((K_ + 511) >> 9)), lane(lane_), pk(0), pseg(0),
-        ps(0), dummy((const u32x4*)dummy_) {
-    prow = nrows > 0 ? (const u32x4*)m.row(0) : dummy;
+  __device__ __forceinline__ RowStream(const Map& m_, int K_, int nrows, int lane_)
+      : m(m_), K(uni(K_)), nseg(uni((K_ + 511) >> 9)), S(uni(nrows * ((K_ + 511) >> 9))),
+        lane16((uint32_t)lane_ * 16u), lane(lane_), ps(0), pseg(0), pk(0) {
+    row = S > 0 ? (const char*)m.row(0) : nullptr;
   }
+  // Weights are read with buffer loads whose descriptor spans exactly the
+  // current row (2K bytes): lanes past a ragged row's end, and every slot
+  // past the end of the stream (descriptor of 0 bytes), read zeros without a
+  // memory access.  So every ring refill is issued unconditionally -- the
+  // compiler can wait for exactly the oldest load -- and costs nothing when
+  // there is nothing to read.
   __device__ __forceinline__ u32x4 next() {
-    // lanes past the row end (K not a multiple of 512) re-read the row's
-    // first 16 bytes and are skipped by the consumer
-    const int ch = pseg * 64 + lane;
-    const u32x4* a = ps < S ? prow + (ch * 8 < K ? ch : 0) : dummy;
-    const u32x4 v = ld_nt16(a);
+    const bool live = ps < S;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), (short)0, live ? 2 * K : 0, (int)kBufFlags);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane16, pseg * 1024, kNT);
     ++ps;
     if (++pseg == nseg) {
       pseg = 0;
       ++pk;
-      if (ps < S) prow = (const u32x4*)m.row(pk);
+      if (ps < S) row = (const char*)m.row(pk);
     }
     return v;
   }
@@ -353,31 +502,32 @@ struct RowStream {
 #pragma unroll
     for (int d = 0; d < RING; ++d) ring[d] = next();
   }
+  // xs must hold finite values (zero) from each row's K up to the next
+  // multiple of 512: lanes past a ragged row's end multiply zero weights
   __device__ __forceinline__ void run(const float* xs, float* out) {
+    const float* xl = xs + lane * 8;
     int ck = 0, cseg = 0;
     float acc0 = 0.f, acc1 = 0.f;
     for (int s0 = 0; s0 < S; s0 += RING) {
 #pragma unroll
       for (int d = 0; d < RING; ++d) {
         if (s0 + d < S) {
-          const int ch = cseg * 64 + lane;
-          if (ch * 8 < K) {
-            const float* xp = xs + m.xoff(ck) + ch * 8;
-            const f32x4 a = *(const f32x4*)xp;
-            const f32x4 b = *(const f32x4*)(xp + 4);
-            const u32x4 w = ring[d];
-            acc0 = fmaf(bf_lo(w.x), a.x, acc0);
-            acc1 = fmaf(bf_hi(w.x), a.y, acc1);
-            acc0 = fmaf(bf_lo(w.y), a.z, acc0);
-            acc1 = fmaf(bf_hi(w.y), a.w, acc1);
-            acc0 = fmaf(bf_lo(w.z), b.x, acc0);
-            acc1 = fmaf(bf_hi(w.z), b.y, acc1);
-            acc0 = fmaf(bf_lo(w.w), b.z, acc0);
-            acc1 = fmaf(bf_hi(w.w), b.w, acc1);
-          }
+          const float* xp = xl + m.xoff(ck) + cseg * 512;
+          const f32x4 a = *(const f32x4*)xp;
+          const f32x4 b = *(const f32x4*)(xp + 4);
+          const u32x4 w = ring[d];
+          acc0 = fmaf(bf_lo(w.x), a.x, acc0);
+          acc1 = fmaf(bf_hi(w.x), a.y, acc1);
+          acc0 = fmaf(bf_lo(w.y), a.z, acc0);
+          acc1 = fmaf(bf_hi(w.y), a.w, acc1);
+          acc0 = fmaf(bf_lo(w.z), b.x, acc0);
+          acc1 = fmaf(bf_hi(w.z), b.y, acc1);
+          acc0 = fmaf(bf_lo(w.w), b.z, acc0);
+          acc1 = fmaf(bf_hi(w.w), b.w, acc1);
           if (++cseg == nseg) {
-            const float v = wave_sum(acc0 + acc1);
-            if (lane == 0) out[m.slot(ck)] = v;
+            // every lane holds the same sum: an unconditional write keeps
+            // the loop free of divergent branches (same value, same address)
+            out[m.slot(ck)] = wave_sum(acc0 + acc1);
             acc0 = 0.f;
             acc1 = 0.f;
             cseg = 0;
@@ -390,234 +540,66 @@ struct RowStream {
   }
 };
 
+// zero xs[n .. n rounded up to 512) (the padding a ragged row length reads)
+__device__ __forceinline__ void pad_zero(Ctx& c, float* x, int n) {
+  const int end = (n + 511) & ~511;
+  for (int i = n + c.tid; i < end; i += kThreads) x[i] = 0.f;
+}
+
 // rows of a tile handled by wavefront w: local rows w, w + kWaves, ...
 __device__ __forceinline__ int wave_rows(int nrows, int w) {
   return nrows > w ? (nrows - w + kWaves - 1) / kWaves : 0;
 }
 
-// one matrix, rows [a, b) of row length K; slot = local row
-struct PlainMap {
-  const uint16_t* W;
-  int a, w, K;
-  __device__ const uint16_t* row(int k) const { return W + (size_t)(a + w + k * kWaves) * K; }
-  __device__ int xoff(int) const { return 0; }
-  __device__ int slot(int k) const { return w + k * kWaves; }
+// Rows of one GEMV instruction, described by data so that every dense
+// opcode runs the same code (one copy of the streaming loop keeps the hot
+// code inside the instruction cache).  Output row r in [a, a + nrows) has R
+// streamed rows (R = 2 pairs gate/up or two experts); streamed row s of r
+// comes from matrix part s, whose rows may be split over up to three
+// pointers at global rows s1 and s2 (Wq|Wk|Wv, or expert a|expert b).
+struct GemvDesc {
+  const uint16_t *b00, *b01, *b02;
+  const uint16_t *b10, *b11, *b12;
+  int s1, s2, K, R, xoff1, a, w;
 };
 
-// two matrices interleaved per local row i: streamed row 2i from X, 2i+1 from
-// Y (x offset xo for Y); slots 2i and 2i+1
-struct PairMap {
-  const uint16_t *X, *Y;
-  int a, w, K, yoff;
+struct GenMap {
+  const GemvDesc& g;
   __device__ const uint16_t* row(int k) const {
-    return psel(k & 1, X, Y) + (size_t)(a + w + (k >> 1) * kWaves) * K;
+    const bool two = g.R == 2;
+    const int j = two ? (k >> 1) : k;
+    const bool s = two && (k & 1);
+    const int r = g.a + g.w + j * kWaves;
+    const bool in1 = r >= g.s1, in2 = r >= g.s2;
+    const int r0 = in2 ? g.s2 : (in1 ? g.s1 : 0);
+    const uint16_t* p0 = psel(in2, psel(in1, g.b00, g.b01), g.b02);
+    const uint16_t* p1 = psel(in2, psel(in1, g.b10, g.b11), g.b12);
+    return psel(s, p0, p1) + (size_t)(r - r0) * g.K;
   }
-  __device__ int xoff(int k) const { return (k & 1) ? yoff : 0; }
-  __device__ int slot(int k) const { return 2 * (w + (k >> 1) * kWaves) + (k & 1); }
+  __device__ int xoff(int k) const { return (g.R == 2 && (k & 1)) ? g.xoff1 : 0; }
+  __device__ int slot(int k) const {
+    return g.R == 2 ? 2 * (g.w + (k >> 1) * kWaves) + (k & 1) : g.w + k * kWaves;
+  }
 };
 
-// ---------------------------------------------------------------- opcode: RMSNorm + QKV
+constexpr int kNoSplit = 0x7fffffff;
 
-struct QkvMap {
-  const uint16_t *wq, *wk, *wv;
-  int a, w, d, qd, kvd;
-  __device__ const uint16_t* row(int k) const {
-    const int r = a + w + k * kWaves;
-    const bool isk = r >= qd, isv = r >= qd + kvd;
-    const int rr = r - (isk ? qd : 0) - (isv ? kvd : 0);
-    return psel(isk, wq, psel(isv, wk, wv)) + (size_t)rr * d;
-  }
-  __device__ int xoff(int) const { return 0; }
-  __device__ int slot(int k) const { return w + k * kWaves; }
-};
-
-// stage the residual entering layer l (the embedding at layer 0) into dst
-// for rows [r0, r1); false on abort
-__device__ __forceinline__ bool fetch_hin(Ctx& c, int l, int r0, int r1, float* dst) {
-  const KParams& p = c.p;
-  if (l == 0) {
-    bool ok;
-    const int tok = step_token(c, &ok);
-    if (!ok) return false;
-    const uint16_t* e = wptr(p, W_EMBED) + (size_t)tok * p.d;
-    for (int i = r0 + c.tid; i < r1; i += kThreads) dst[i - r0] = bf_val(ld_u16(e + i));
-  } else {
-    ll_fetch(c, p.h + r0, r1 - r0, tag_of(p, c.t, l), dst);
-  }
+// the embedding row of this step's token, rows [r0, r1), into dst
+__device__ __forceinline__ bool embed_rows(Ctx& c, int r0, int r1, float* dst) {
+  CKParams& p = c.p;
+  bool ok;
+  const int tok = step_token(c, &ok);
+  if (!ok) return false;
+  const uint16_t* e = wptr(p, W_EMBED) + (size_t)tok * p.d;
+  for (int i = r0 + c.tid; i < r1; i += kThreads) dst[i - r0] = bf_val(ld_u16(e + i));
   return true;
 }
-
-__device__ __forceinline__ bool op_qkv(Ctx& c, int l, int a, int b) {
-  const KParams& p = c.p;
-  const QkvMap m{lptr(p, l, WL_Q), lptr(p, l, WL_K), lptr(p, l, WL_V), a, c.wave, p.d, p.qd, p.kvd};
-  RowStream<QkvMap> rs(m, p.d, wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  if (!fetch_hin(c, l, 0, p.d, c.xs)) return false;
-  if (!sync_ok(c)) return false;
-  rmsnorm_lds(c, p.d, lptr(p, l, WL_ATTN_NORM));
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  const uint32_t tag = tag_of(p, c.t, l);
-  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.qkv + a + i, c.out[i], tag);
-  return true;
-}
-
-// ---------------------------------------------------------------- opcode: O-proj + residual
-
-__device__ __forceinline__ bool op_oproj(Ctx& c, int l, int a, int b) {
-  const KParams& p = c.p;
-  const PlainMap m{lptr(p, l, WL_O), a, c.wave, p.qd};
-  RowStream<PlainMap> rs(m, p.qd, wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  if (!fetch_hin(c, l, a, b, c.res)) return false;
-  ll_fetch(c, p.aout, p.qd, tag_of(p, c.t, l), c.xs);
-  if (!sync_ok(c)) return false;
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  const uint32_t tag = tag_of(p, c.t, l);
-  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.hmid + a + i, c.res[i] + c.out[i], tag);
-  return true;
-}
-
-// ---------------------------------------------------------------- opcode: RMSNorm + up/gate + SiLU
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ bool op_upgate(Ctx& c, int l, int a, int b) {
-  const KParams& p = c.p;
-  const PairMap m{lptr(p, l, WL_GATE), lptr(p, l, WL_UP), a, c.wave, p.d, 0};
-  RowStream<PairMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  ll_fetch(c, p.hmid, p.d, tag_of(p, c.t, l), c.xs);
-  if (!sync_ok(c)) return false;
-  rmsnorm_lds(c, p.d, lptr(p, l, WL_FFN_NORM));
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  const uint32_t tag = tag_of(p, c.t, l);
-  for (int i = c.tid; i < b - a; i += kThreads)
-    ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
-  return true;
-}
-
-// ---------------------------------------------------------------- opcode: down + residual
-
-__device__ __forceinline__ bool op_down(Ctx& c, int l, int a, int b) {
-  const KParams& p = c.p;
-  const PlainMap m{lptr(p, l, WL_DOWN), a, c.wave, p.F};
-  RowStream<PlainMap> rs(m, p.F, wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  ll_fetch(c, p.hmid + a, b - a, tag_of(p, c.t, l), c.res);
-  ll_fetch(c, p.act, p.F, tag_of(p, c.t, l), c.xs);
-  if (!sync_ok(c)) return false;
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  const uint32_t tag = tag_of(p, c.t, l + 1);
-  for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.h + a + i, c.res[i] + c.out[i], tag);
-  return true;
-}
-
-// ---------------------------------------------------------------- opcodes: MoE
-
-// expert-rows r in [a, b) of the top_k * F stacked rows: r < F is expert a's
-// row r, else expert b's row r - F; streamed rows alternate gate and up
-struct MoeUpMap {
-  const uint16_t *ga, *ua, *gb, *ub;
-  int a, w, d, F;
-  __device__ const uint16_t* row(int k) const {
-    const int r = a + w + (k >> 1) * kWaves;
-    const bool second = r >= F;
-    const int rr = second ? r - F : r;
-    return psel(k & 1, psel(second, ga, gb), psel(second, ua, ub)) + (size_t)rr * d;
-  }
-  __device__ int xoff(int) const { return 0; }
-  __device__ int slot(int k) const { return 2 * (w + (k >> 1) * kWaves) + (k & 1); }
-};
-
-__device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int index) {
-  const KParams& p = c.p;
-  const uint32_t tag = tag_of(p, c.t, l);
-  ll_fetch(c, p.hmid, p.d, tag, c.xs);
-  if (!sync_ok(c)) return false;
-  rmsnorm_lds(c, p.d, lptr(p, l, WL_FFN_NORM));
-  // router logits: one wavefront per expert row
-  const uint16_t* wr = lptr(p, l, WL_ROUTER);
-  for (int e = c.wave; e < p.E; e += kWaves) {
-    float acc = 0.f;
-    for (int i = c.lane; i < p.d; i += 64) acc = fmaf(bf_val(ld_u16(wr + (size_t)e * p.d + i)), c.xs[i], acc);
-    const float z = wave_sum(acc);
-    if (c.lane == 0) c.red[64 + e] = z;
-  }
-  __syncthreads();
-  if (c.tid == 0) {
-    // top-2: larger logit first, lower expert index on ties
-    int ea = 0;
-    for (int e = 1; e < p.E; ++e)
-      if (c.red[64 + e] > c.red[64 + ea]) ea = e;
-    int eb = ea == 0 ? 1 : 0;
-    for (int e = 0; e < p.E; ++e)
-      if (e != ea && c.red[64 + e] > c.red[64 + eb]) eb = e;
-    const float za = c.red[64 + ea], zb = c.red[64 + eb];
-    const float q = expf(zb - za);
-    c.sflag[3] = ea;
-    c.sflag[4] = eb;
-    if (index == 0) {
-      ll_store(p.route + 0, __int_as_float(ea), tag);
-      ll_store(p.route + 1, __int_as_float(eb), tag);
-      ll_store(p.route + 2, 1.0f / (1.0f + q), tag);
-      ll_store(p.route + 3, q / (1.0f + q), tag);
-    }
-  }
-  __syncthreads();
-  const int ea = c.sflag[3], eb = c.sflag[4];
-  const MoeUpMap m{lptr(p, l, WL_EXPERTS + ea), lptr(p, l, WL_EXPERTS + p.E + ea),
-                   lptr(p, l, WL_EXPERTS + eb), lptr(p, l, WL_EXPERTS + p.E + eb), a, c.wave, p.d, p.F};
-  RowStream<MoeUpMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  for (int i = c.tid; i < b - a; i += kThreads)
-    ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
-  return true;
-}
-
-__device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
-  const KParams& p = c.p;
-  const uint32_t tag = tag_of(p, c.t, l);
-  ll_fetch(c, p.route, 4, tag, c.red + 8);
-  ll_fetch(c, p.hmid + a, b - a, tag, c.res);
-  ll_fetch(c, p.act, 2 * p.F, tag, c.xs);
-  if (!sync_ok(c)) return false;
-  const int ea = __float_as_int(c.red[8]), eb = __float_as_int(c.red[9]);
-  const float wa = c.red[10], wb = c.red[11];
-  if (ea < 0 || ea >= p.E || eb < 0 || eb >= p.E) {
-    if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
-    __syncthreads();
-    return false;
-  }
-  const PairMap m{lptr(p, l, WL_EXPERTS + 2 * p.E + ea), lptr(p, l, WL_EXPERTS + 2 * p.E + eb), a,
-                  c.wave, p.F, p.F};
-  RowStream<PairMap> rs(m, p.F, 2 * wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  rs.run(c.xs, c.out);
-  __syncthreads();
-  const uint32_t otag = tag_of(p, c.t, l + 1);
-  for (int i = c.tid; i < b - a; i += kThreads)
-    ll_store(p.h + a + i, c.res[i] + (wa * c.out[2 * i] + wb * c.out[2 * i + 1]), otag);
-  return true;
-}
-
-// ---------------------------------------------------------------- opcode: LM head
-
-__device__ __forceinline__ bool op_lmhead(Ctx& c, int a, int b, int index) {
-  const KParams& p = c.p;
-  const PlainMap m{wptr(p, p.tied ? W_EMBED : W_LM_HEAD), a, c.wave, p.d};
-  RowStream<PlainMap> rs(m, p.d, wave_rows(b - a, c.wave), c.lane, p.sched);
-  rs.prefetch();
-  ll_fetch(c, p.h, p.d, tag_of(p, c.t, p.L), c.xs);
-  if (!sync_ok(c)) return false;
-  rmsnorm_lds(c, p.d, wptr(p, W_FINAL_NORM));
-  rs.run(c.xs, c.out);
-  __syncthreads();
+// LM-head epilogue: logits out, and this tile's (max, lowest argmax)
+__device__ __forceinline__ void lmhead_epilogue(Ctx& c, int a, int b, int index) {
+  CKParams& p = c.p;
   float* logits = p.logits_out ? p.logits_out + (size_t)c.t * p.V + a : nullptr;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -656,6 +638,193 @@ __device__ __forceinline__ bool op_lmhead(Ctx& c, int a, int b, int index) {
     ll_store(p.lm + 2 * index + 1, __int_as_float(bi), tag);
   }
   __syncthreads();
+}
+
+// RMSNorm + QKV, O-proj + residual, RMSNorm + gate/up + SiLU, down + residual
+// and RMSNorm + LM head: one code path, the opcode only picks matrices,
+// inputs and the epilogue.  Weights for the first RING loads per lane are
+// requested before the inputs are waited for.
+__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  GemvDesc g;
+  g.b00 = g.b01 = g.b02 = g.b10 = g.b11 = g.b12 = nullptr;
+  g.s1 = g.s2 = kNoSplit;
+  g.R = 1;
+  g.xoff1 = 0;
+  g.a = a;
+  g.w = c.wave;
+  const uint16_t* gamma = nullptr;
+  const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
+  Fetch f[2] = {{p.h, 0, tag, c.xs}, {p.h, 0, tag, c.res}};
+  bool embed_x = false, embed_res = false;
+  switch (op) {
+    case OP_QKV:
+      g.b00 = lptr(p, l, WL_Q); g.b01 = lptr(p, l, WL_K); g.b02 = lptr(p, l, WL_V);
+      g.s1 = p.qd; g.s2 = p.qd + p.kvd; g.K = p.d;
+      gamma = lptr(p, l, WL_ATTN_NORM);
+      if (l == 0) embed_x = true;
+      else f[0] = {p.h, p.d, tag, c.xs};
+      break;
+    case OP_OPROJ:
+      g.b00 = lptr(p, l, WL_O); g.K = p.qd;
+      f[0] = {p.aout, p.qd, tag, c.xs};
+      if (l == 0) embed_res = true;
+      else f[1] = {p.h + a, b - a, tag, c.res};   // published by the previous layer
+      break;
+    case OP_UPGATE:
+      g.b00 = lptr(p, l, WL_GATE); g.b10 = lptr(p, l, WL_UP); g.R = 2; g.K = p.d;
+      gamma = lptr(p, l, WL_FFN_NORM);
+      f[0] = {p.hmid, p.d, tag, c.xs};
+      break;
+    case OP_DOWN:
+      g.b00 = lptr(p, l, WL_DOWN); g.K = p.F;
+      f[0] = {p.act, p.F, tag, c.xs};
+      f[1] = {p.hmid + a, b - a, tag, c.res};
+      break;
+    default:  // OP_LMHEAD
+      g.b00 = wptr(p, p.tied ? W_EMBED : W_LM_HEAD); g.K = p.d;
+      gamma = wptr(p, W_FINAL_NORM);
+      f[0] = {p.h, p.d, tag, c.xs};
+      break;
+  }
+  const GenMap m{g};
+  RowStream<GenMap> rs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane);
+  rs.prefetch();
+  const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
+  if (embed_x) {
+    // the token comes from the previous step's LM-head partials (it waits on
+    // them itself); the embedding row is a plain read
+    if (!embed_rows(c, 0, p.d, c.xs)) return false;
+    mark_ready(c);
+    __syncthreads();
+  } else {
+    if (embed_res && !embed_rows(c, a, b, c.res)) return false;
+    if (!gather_inputs<2>(c, f)) return false;
+  }
+  if (g.K & 511) {
+    pad_zero(c, c.xs, g.K);
+    __syncthreads();
+  }
+  if (gamma) rmsnorm_g(c, p.d, gamma, gr);
+  rs.run(c.xs, c.out);
+  mark_computed(c);
+  __syncthreads();
+  switch (op) {
+    case OP_QKV:
+      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.qkv + a + i, c.out[i], tag);
+      break;
+    case OP_OPROJ:
+      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.hmid + a + i, c.res[i] + c.out[i], tag);
+      break;
+    case OP_UPGATE:
+      for (int i = c.tid; i < b - a; i += kThreads)
+        ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
+      break;
+    case OP_DOWN: {
+      const uint32_t otag = tag_of(p, c.t, l + 1);
+      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.h + a + i, c.res[i] + c.out[i], otag);
+      break;
+    }
+    default:
+      lmhead_epilogue(c, a, b, index);
+      break;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------- opcodes: MoE
+
+__device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, l);
+  const uint16_t* gamma = lptr(p, l, WL_FFN_NORM);
+  const Gains gr = load_gains(c, p.d, gamma);
+  const Fetch f[1] = {{p.hmid, p.d, tag, c.xs}};
+  if (!gather_inputs<1>(c, f)) return false;
+  rmsnorm_g(c, p.d, gamma, gr);
+  if (p.d & 511) {
+    pad_zero(c, c.xs, p.d);
+    __syncthreads();
+  }
+  // router logits: one wavefront per expert row
+  const uint16_t* wr = lptr(p, l, WL_ROUTER);
+  for (int e = c.wave; e < p.E; e += kWaves) {
+    float acc = 0.f;
+    for (int i = c.lane; i < p.d; i += 64) acc = fmaf(bf_val(ld_u16(wr + (size_t)e * p.d + i)), c.xs[i], acc);
+    const float z = wave_sum(acc);
+    if (c.lane == 0) c.red[64 + e] = z;
+  }
+  __syncthreads();
+  if (c.tid == 0) {
+    // top-2: larger logit first, lower expert index on ties
+    int ea = 0;
+    for (int e = 1; e < p.E; ++e)
+      if (c.red[64 + e] > c.red[64 + ea]) ea = e;
+    int eb = ea == 0 ? 1 : 0;
+    for (int e = 0; e < p.E; ++e)
+      if (e != ea && c.red[64 + e] > c.red[64 + eb]) eb = e;
+    const float za = c.red[64 + ea], zb = c.red[64 + eb];
+    const float q = expf(zb - za);
+    c.sflag[3] = ea;
+    c.sflag[4] = eb;
+    if (index == 0) {
+      ll_store(p.route + 0, __int_as_float(ea), tag);
+      ll_store(p.route + 1, __int_as_float(eb), tag);
+      ll_store(p.route + 2, 1.0f / (1.0f + q), tag);
+      ll_store(p.route + 3, q / (1.0f + q), tag);
+    }
+  }
+  __syncthreads();
+  const int ea = uni(c.sflag[3]), eb = uni(c.sflag[4]);
+  // expert-rows r < F are expert a's rows, r >= F expert b's row r - F;
+  // streamed rows alternate gate and up
+  GemvDesc g;
+  g.b00 = lptr(p, l, WL_EXPERTS + ea); g.b01 = lptr(p, l, WL_EXPERTS + eb); g.b02 = nullptr;
+  g.b10 = lptr(p, l, WL_EXPERTS + p.E + ea); g.b11 = lptr(p, l, WL_EXPERTS + p.E + eb); g.b12 = nullptr;
+  g.s1 = p.F; g.s2 = kNoSplit; g.K = p.d; g.R = 2; g.xoff1 = 0; g.a = a; g.w = c.wave;
+  const GenMap m{g};
+  RowStream<GenMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane);
+  rs.prefetch();
+  rs.run(c.xs, c.out);
+  mark_computed(c);
+  __syncthreads();
+  for (int i = c.tid; i < b - a; i += kThreads)
+    ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
+  return true;
+}
+
+__device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
+  CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, l);
+  const int Fpad = (p.F + 511) & ~511;
+  const Fetch f[4] = {{p.route, 4, tag, c.red + 8}, {p.act, p.F, tag, c.xs},
+                      {p.act + p.F, p.F, tag, c.xs + Fpad}, {p.hmid + a, b - a, tag, c.res}};
+  if (p.F & 511) {
+    pad_zero(c, c.xs, p.F);
+    pad_zero(c, c.xs + Fpad, p.F);
+  }
+  if (!gather_inputs<4>(c, f)) return false;
+  const int ea = uni(__float_as_int(c.red[8])), eb = uni(__float_as_int(c.red[9]));
+  const float wa = __int_as_float(uni(__float_as_int(c.red[10])));
+  const float wb = __int_as_float(uni(__float_as_int(c.red[11])));
+  if (ea < 0 || ea >= p.E || eb < 0 || eb >= p.E) {
+    if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
+    __syncthreads();
+    return false;
+  }
+  GemvDesc g;
+  g.b00 = lptr(p, l, WL_EXPERTS + 2 * p.E + ea); g.b01 = g.b02 = nullptr;
+  g.b10 = lptr(p, l, WL_EXPERTS + 2 * p.E + eb); g.b11 = g.b12 = nullptr;
+  g.s1 = g.s2 = kNoSplit; g.K = p.F; g.R = 2; g.xoff1 = Fpad; g.a = a; g.w = c.wave;
+  const GenMap m{g};
+  RowStream<GenMap> rs(m, p.F, 2 * wave_rows(b - a, c.wave), c.lane);
+  rs.prefetch();
+  rs.run(c.xs, c.out);
+  mark_computed(c);
+  __syncthreads();
+  const uint32_t otag = tag_of(p, c.t, l + 1);
+  for (int i = c.tid; i < b - a; i += kThreads)
+    ll_store(p.h + a + i, c.res[i] + (wa * c.out[2 * i] + wb * c.out[2 * i + 1]), otag);
   return true;
 }
 
@@ -684,7 +853,7 @@ __device__ __forceinline__ void merge_into(AttnState<G>& s, const float* om, con
 
 template <int HD, int G>
 __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
-  const KParams& p = c.p;
+  CKParams& p = c.p;
   constexpr int LPR = HD / 8;     // lanes per K/V row
   constexpr int PPW = 64 / LPR;   // positions per wavefront load
   const int pos = p.start_pos + c.t;
@@ -725,19 +894,22 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   float* vs = ks + HD;              // [HD]
   float* wst = vs + HD;             // [kWaves][G][HD + 2] per-wave states
   const uint32_t tag = tag_of(p, c.t, l);
-  ll_fetch(c, p.qkv + kvh * G * HD, G * HD, tag, qs);
-  ll_fetch(c, p.qkv + p.qd + kvh * HD, HD, tag, ks);
-  ll_fetch(c, p.qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs);
-  if (!sync_ok(c)) return false;
+  // this thread's RoPE pair (one of (G + 1) * HD/2 <= kThreads), read before
+  // the inputs are waited for
+  static_assert((G + 1) * (HD / 2) <= kThreads, "one RoPE pair per thread");
+  const int re = c.tid < (G + 1) * (HD / 2) ? c.tid : 0;
+  const float cs = ld_f32(p.rope + (size_t)pos * (HD / 2) + re % (HD / 2));
+  const float sn = ld_f32(p.rope + (size_t)p.max_seq * (HD / 2) + (size_t)pos * (HD / 2) + re % (HD / 2));
+  const Fetch f[3] = {{p.qkv + kvh * G * HD, G * HD, tag, qs},
+                      {p.qkv + p.qd + kvh * HD, HD, tag, ks},
+                      {p.qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
+  if (!gather_inputs<3>(c, f)) return false;
 
   // RoPE (pairs i, i + HD/2) on q heads and k; q pre-scaled for exp2 softmax
-  const float* cosr = p.rope + (size_t)pos * (HD / 2);
-  const float* sinr = p.rope + (size_t)p.max_seq * (HD / 2) + (size_t)pos * (HD / 2);
   const float qscale = 1.4426950408889634f / sqrtf((float)HD);
-  for (int e = c.tid; e < (G + 1) * (HD / 2); e += kThreads) {
-    const int h = e / (HD / 2), i = e % (HD / 2);
+  if (c.tid < (G + 1) * (HD / 2)) {
+    const int h = c.tid / (HD / 2), i = c.tid % (HD / 2);
     float* x = h < G ? qs + h * HD : ks;
-    const float cs = ld_f32(cosr + i), sn = ld_f32(sinr + i);
     const float x0 = x[i], x1 = x[i + HD / 2];
     float y0 = x0 * cs - x1 * sn;
     float y1 = x1 * cs + x0 * sn;
@@ -908,11 +1080,11 @@ __device__ __forceinline__ bool op_attn_hd(Ctx& c, int l, int kvh, int chunk) {
 // ---------------------------------------------------------------- opcode: split-KV reduction
 
 __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
-  const KParams& p = c.p;
+  CKParams& p = c.p;
   const int HD = p.hd, n = p.n_chunks, W = HD + 2;
   const uint32_t tag = tag_of(p, c.t, l);
-  ll_fetch(c, p.part + (size_t)qh * n * W, n * W, tag, c.xs);
-  if (!sync_ok(c)) return false;
+  const Fetch f[1] = {{p.part + (size_t)qh * n * W, n * W, tag, c.xs}};
+  if (!gather_inputs<1>(c, f)) return false;
   for (int i = c.tid; i < HD; i += kThreads) {
     float M = -INFINITY;
     for (int k = 0; k < n; ++k) M = fmaxf(M, c.xs[k * W]);
@@ -937,7 +1109,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
   // are the first and only argument): referring to the by-value parameter
   // itself would make the compiler copy it to scratch memory.
   (void)params;
-  const KParams* pk = (const KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  CKParams* pk = (CKParams*)__builtin_amdgcn_kernarg_segment_ptr();
   extern __shared__ __align__(16) float smem[];
   volatile int* sflag = s_flags;
   const int wg = blockIdx.x;
@@ -947,46 +1119,50 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
     sflag[2] = -1;
   }
   __syncthreads();
-  const int n = ld_i32(pk->sched + kWords + wg);
+  const int n = ldc_i32(pk->sched + kWords + wg);
   bool ok = true;
   for (int t = 0; t < pk->n_steps && ok; ++t) {
     for (int i = 0; i < n && ok; ++i) {
       // Opaque copies of the parameter pointer and thread id: nothing that
       // depends on them is hoisted out of the persistent loop, so values one
       // opcode needs do not stay live (and spill) through all the others.
-      const KParams* pp = pk;
+      CKParams* pp = pk;
       int tid = threadIdx.x;
       asm volatile("" : "+s"(pp));
       asm volatile("" : "+v"(tid));
-      const KParams& p = *pp;
-      Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
-            sflag, wg, i, t, tid, tid & 63, tid >> 6};
+      CKParams& p = *pp;
       const int32_t* ins = p.sched + kWords + p.n_wg + ((size_t)wg * p.max_instr + i) * kWords;
-      const int op = ld_i32(ins + I_OP), l = ld_i32(ins + I_LAYER), a = ld_i32(ins + I_A),
-                b = ld_i32(ins + I_B), index = ld_i32(ins + I_INDEX);
-      uint64_t* tr = p.trace ? p.trace + (((size_t)wg * p.n_steps + t) * p.max_instr + i) * 2 : nullptr;
+      const int op = ldc_i32(ins + I_OP), l = ldc_i32(ins + I_LAYER), a = ldc_i32(ins + I_A),
+                b = ldc_i32(ins + I_B), index = ldc_i32(ins + I_INDEX);
+      uint64_t* tr = p.trace ? p.trace + (((size_t)wg * p.n_steps + t) * p.max_instr + i) * kTraceWords
+                             : nullptr;
+      Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
+            sflag, wg, i, t, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6),
+            ldc_i32(ins + I_STAGE), index, ldc_i32(ins + I_WAIT_STAGE), ldc_i32(ins + I_WAIT_COUNT),
+            ldc_i32(ins + I_WAIT_PREV), tr};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
       switch (op) {
-        case OP_QKV: ok = op_qkv(c, l, a, b); break;
+        case OP_QKV:
+        case OP_OPROJ:
+        case OP_UPGATE:
+        case OP_DOWN:
+        case OP_LMHEAD: ok = op_gemv(c, op, l, a, b, index); break;
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
-        case OP_OPROJ: ok = op_oproj(c, l, a, b); break;
-        case OP_UPGATE: ok = op_upgate(c, l, a, b); break;
-        case OP_DOWN: ok = op_down(c, l, a, b); break;
         case OP_MOE_UPGATE: ok = op_moe_upgate(c, l, a, b, index); break;
         case OP_MOE_DOWN: ok = op_moe_down(c, l, a, b); break;
-        case OP_LMHEAD: ok = op_lmhead(c, a, b, index); break;
         default: break;
       }
-      if (tr && tid == 0) st_u64(tr + 1, wall_clock64());
+      if (ok) signal_done(c);
     }
   }
   // the last step's argmax
   if (ok && wg == 0) {
-    const KParams& p = *pk;
+    CKParams& p = *pk;
     const int tid = threadIdx.x;
     Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
-          sflag, wg, 0, p.n_steps, tid, tid & 63, tid >> 6};
+          sflag, wg, 0, p.n_steps, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6), 0, 0, 0, 0,
+          0, nullptr};
     bool fok;
     const int am = fold_argmax(c, p.n_steps - 1, &fok);
     if (fok && tid == 0) st_i32(p.tokens_out + p.n_steps - 1, am);
@@ -1024,7 +1200,7 @@ int max_coop_blocks(int device, size_t lds, int* out) {
   return MKD_OK;
 }
 
-int launch(const KParams& p, size_t ll_words, void* stream, const char** why) {
+int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why) {
   hipStream_t s = (hipStream_t)stream;
   const size_t lds = lds_bytes(p);
   int blocks = (int)((ll_words + 255) / 256);
@@ -1040,6 +1216,7 @@ int launch(const KParams& p, size_t ll_words, void* stream, const char** why) {
   }
   KParams pc = p;
   void* args[] = {&pc};
+  if (ev0 && hipEventRecord((hipEvent_t)ev0, s) != hipSuccess) { *why = "hipEventRecord"; return MKD_E_HIP; }
   const hipError_t e = hipLaunchCooperativeKernel((const void*)mkd_megakernel, dim3(p.n_wg),
                                                   dim3(kThreads), args, (unsigned)lds, s);
   if (e == hipErrorCooperativeLaunchTooLarge) {
@@ -1050,6 +1227,7 @@ int launch(const KParams& p, size_t ll_words, void* stream, const char** why) {
     *why = hipGetErrorString(e);
     return MKD_E_HIP;
   }
+  if (ev1 && hipEventRecord((hipEvent_t)ev1, s) != hipSuccess) { *why = "hipEventRecord"; return MKD_E_HIP; }
   return MKD_OK;
 }
 

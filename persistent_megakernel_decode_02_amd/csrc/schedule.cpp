@@ -1,14 +1,18 @@
-// Host-side schedule builder and validator (schedule spec v1).
+// Host-side schedule builder and validator (schedule spec v2).
 //
 // The persistent kernel walks a host-built list of every operation of the
 // forward pass (Hyperkernel teardown, "What a megakernel buys"; Kittens VM
 // summary, "Method").  The pages fix no format, tiling or assignment; this
-// file implements this library's spec v1:
+// file implements this library's spec v2:
 //   stages per token: per layer QKV, ATTN, [AREDUCE if n_chunks > 1], OPROJ,
 //   UPGATE|MOE_UPGATE, DOWN|MOE_DOWN; then LMHEAD.
 //   GEMV stage over R rows: n = min(n_wg, R) tiles, tile i = [i*R/n, (i+1)*R/n).
 //   ATTN: hkv * n_chunks instructions (kv_head = i / n_chunks, chunk = i % n_chunks).
-//   AREDUCE: hq instructions.  Instruction i of a stage runs on block i % n_wg.
+//   AREDUCE: hq instructions.  Instruction i of a stage runs on block
+//   (offset + i) % n_wg; the offset is 0 except for OPROJ, whose tiles skip
+//   the blocks that ran the stage before it (ATTN, or AREDUCE) when there
+//   are more blocks than that stage has instructions: those blocks finish
+//   attention late, and an O-projection tile there would hold the stage up.
 #include <string.h>
 
 #include <vector>
@@ -80,6 +84,19 @@ static int stage_ninstr(const StageDesc& s, int n_wg) {
   return s.size;
 }
 
+// blocks stage s may use, and the first of them
+void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, int* first) {
+  *avail = n_wg;
+  *first = 0;
+  if (st[s].op == OP_OPROJ && s > 0) {
+    const int prev = st[s - 1].size;  // ATTN or AREDUCE instruction count
+    if (n_wg > prev) {
+      *avail = n_wg - prev;
+      *first = prev;
+    }
+  }
+}
+
 static void operands(const StageDesc& s, int n_wg, int n_chunks, int i, int32_t* a, int32_t* b) {
   if (is_gemv(s.op)) {
     const int64_t n = stage_ninstr(s, n_wg), R = s.size;
@@ -105,13 +122,15 @@ int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, si
   std::vector<StageDesc> st(n_st);
   int got = 0;
   stage_list(c, n_chunks, st.data(), &got, n_st);
-  std::vector<int> cnt(n_st);
-  for (int s = 0; s < n_st; ++s) cnt[s] = stage_ninstr(st[s], n_wg);
-  // per-block instruction counts: block w gets indices i = w, w + n_wg, ...
+  std::vector<int> cnt(n_st), avail(n_st), first(n_st);
+  for (int s = 0; s < n_st; ++s) {
+    placement(st, s, n_wg, &avail[s], &first[s]);
+    cnt[s] = stage_ninstr(st[s], avail[s]);
+  }
   std::vector<int> per_wg(n_wg, 0);
   int64_t total = 0;
   for (int s = 0; s < n_st; ++s) {
-    for (int w = 0; w < n_wg; ++w) per_wg[w] += cnt[s] > w ? (cnt[s] - w + n_wg - 1) / n_wg : 0;
+    for (int i = 0; i < cnt[s]; ++i) ++per_wg[(first[s] + i) % n_wg];
     total += cnt[s];
   }
   int max_instr = 0;
@@ -133,13 +152,13 @@ int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, si
   for (int s = 0; s < n_st; ++s) {
     const int ws = s == 0 ? n_st - 1 : s - 1;
     for (int i = 0; i < cnt[s]; ++i) {
-      const int w = i % n_wg;
+      const int w = (first[s] + i) % n_wg;
       int32_t* ins = body + ((size_t)w * max_instr + fill[w]++) * kWords;
       ins[I_OP] = st[s].op;
       ins[I_LAYER] = st[s].layer;
       ins[I_STAGE] = s;
       ins[I_INDEX] = i;
-      operands(st[s], n_wg, n_chunks, i, &ins[I_A], &ins[I_B]);
+      operands(st[s], avail[s], n_chunks, i, &ins[I_A], &ins[I_B]);
       ins[I_WAIT_STAGE] = ws;
       ins[I_WAIT_COUNT] = cnt[ws];
       ins[I_WAIT_PREV] = s == 0 ? 1 : 0;
@@ -167,8 +186,11 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
   std::vector<StageDesc> st(n_st);
   int got = 0;
   stage_list(c, n_chunks, st.data(), &got, n_st);
-  std::vector<int> cnt(n_st);
-  for (int s = 0; s < n_st; ++s) cnt[s] = stage_ninstr(st[s], n_wg);
+  std::vector<int> cnt(n_st), avail(n_st), first(n_st);
+  for (int s = 0; s < n_st; ++s) {
+    placement(st, s, n_wg, &avail[s], &first[s]);
+    cnt[s] = stage_ninstr(st[s], avail[s]);
+  }
   std::vector<std::vector<char>> seen(n_st);
   for (int s = 0; s < n_st; ++s) seen[s].assign(cnt[s], 0);
   const int32_t* counts = w + kWords;
@@ -185,11 +207,11 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
       if (s < prev) { *why = "a block's list is not in stage order"; return MKD_E_INVALID; }
       prev = s;
       const int i = ins[I_INDEX];
-      if (i < 0 || i >= cnt[s] || i % n_wg != b) { *why = "instruction index or block"; return MKD_E_INVALID; }
+      if (i < 0 || i >= cnt[s] || (first[s] + i) % n_wg != b) { *why = "instruction index or block"; return MKD_E_INVALID; }
       if (seen[s][i]) { *why = "instruction repeated"; return MKD_E_INVALID; }
       seen[s][i] = 1;
       int32_t a, bb;
-      operands(st[s], n_wg, n_chunks, i, &a, &bb);
+      operands(st[s], avail[s], n_chunks, i, &a, &bb);
       if (ins[I_A] != a || ins[I_B] != bb) { *why = "operands differ from the spec"; return MKD_E_INVALID; }
       const int ws = s == 0 ? n_st - 1 : s - 1;
       if (ins[I_WAIT_STAGE] != ws || ins[I_WAIT_COUNT] != cnt[ws] || ins[I_WAIT_PREV] != (s == 0) ||
