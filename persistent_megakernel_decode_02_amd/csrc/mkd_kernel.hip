@@ -27,6 +27,8 @@
 // Wavefront reductions use DPP row permutes plus readlane.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "mkd_internal.h"
 
@@ -1217,8 +1219,19 @@ int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1
   KParams pc = p;
   void* args[] = {&pc};
   if (ev0 && hipEventRecord((hipEvent_t)ev0, s) != hipSuccess) { *why = "hipEventRecord"; return MKD_E_HIP; }
-  const hipError_t e = hipLaunchCooperativeKernel((const void*)mkd_megakernel, dim3(p.n_wg),
-                                                  dim3(kThreads), args, (unsigned)lds, s);
+  // MKD_LAUNCH=plain dispatches the same grid without the cooperative flag.  The
+  // grid was already checked to fit co-resident (max_coop_blocks), so on an idle
+  // device every workgroup is resident at once either way; the switch exists for
+  // profilers that cannot finish their output after a cooperative dispatch.
+  static const bool plain = [] {
+    const char* v = getenv("MKD_LAUNCH");
+    return v && strcmp(v, "plain") == 0;
+  }();
+  const hipError_t e =
+      plain ? hipLaunchKernel((const void*)mkd_megakernel, dim3(p.n_wg), dim3(kThreads), args,
+                              (unsigned)lds, s)
+            : hipLaunchCooperativeKernel((const void*)mkd_megakernel, dim3(p.n_wg), dim3(kThreads),
+                                         args, (unsigned)lds, s);
   if (e == hipErrorCooperativeLaunchTooLarge) {
     *why = "grid does not fit co-resident on the device";
     return MKD_E_COOPERATIVE;
