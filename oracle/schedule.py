@@ -5,9 +5,9 @@ each block reads a host-built instruction tensor to decide its next work
 (Kittens VM summary, "Method"); the blocks get "a schedule of every operation
 in the forward pass" and synchronise on the device (Hyperkernel teardown,
 "What a megakernel buys").  The pages fix no format, tiling or assignment, so
-the tensor below is this project's own specification ("schedule spec v1",
-written out in the design notes, "schedule spec v2"); the GPU library's C++ builder must produce
-the same bytes.
+the tensor below is this project's own specification ("schedule spec v2",
+also written out in the design notes); the GPU library's C++ builder must
+produce the same bytes.
 
 Spec v2 (all int32):
 
