@@ -5,19 +5,20 @@ each block reads a host-built instruction tensor to decide its next work
 (Kittens VM summary, "Method"); the blocks get "a schedule of every operation
 in the forward pass" and synchronise on the device (Hyperkernel teardown,
 "What a megakernel buys").  The pages fix no format, tiling or assignment, so
-the tensor below is this project's own specification ("schedule spec v2",
+the tensor below is this project's own specification ("schedule spec v3",
 also written out in the design notes); the GPU library's C++ builder must
 produce the same bytes.
 
-Spec v2 (all int32):
+Spec v3 (all int32):
 
 * stage order per token: for each layer ``QKV, ATTN, [AREDUCE if n_chunks > 1],
   OPROJ, UPGATE|MOE_UPGATE, DOWN|MOE_DOWN``; then ``LMHEAD``.
-* a GEMV stage over R rows has ``n = min(n_wg, R)`` tiles; tile i covers rows
-  ``[i*R//n, (i+1)*R//n)``.  R: QKV = qd + 2 kvd, OPROJ = DOWN = MOE_DOWN = d,
-  UPGATE = F, MOE_UPGATE = top_k * F, LMHEAD = V.
-* ATTN has ``hkv * n_chunks`` instructions (kv_head = i // n_chunks,
-  chunk = i % n_chunks); AREDUCE has hq (q_head = i).
+* a row-tiled stage over R rows has ``n = min(n_wg, R)`` tiles; tile i covers
+  rows ``[i*R//n, (i+1)*R//n)``.  R: QKV = qd + 2 kvd, OPROJ = DOWN =
+  MOE_DOWN = d, UPGATE = F, MOE_UPGATE = top_k * F, LMHEAD = V.
+* ATTN: with one chunk, one instruction per q head (a = q head, b = 0); with
+  several, one per (kv head, chunk) serving the kv head's q heads together
+  (a = kv head, b = chunk), and AREDUCE has hq (a = q head) merging them.
 * instruction i of a stage goes to block ``(offset + i) % n_wg``; a block's
   list is the concatenation of its instructions in stage order.  The offset
   is 0 except for OPROJ: its tiles skip the blocks that ran the stage just
@@ -29,10 +30,10 @@ Spec v2 (all int32):
   d, hq, hkv, hd, F, V, E, top_k, total_instr}; counts[n_wg]; then
   ``[n_wg][max_instr][16]`` with instruction = {opcode, layer, stage, index,
   a, b, wait_stage, wait_count, wait_prev_token, signal_stage, 0...};
-  ``a, b`` = row range (GEMV), (kv_head, chunk) (ATTN), (q_head, 0)
-  (AREDUCE); ``wait_stage`` is the stage whose outputs the instruction reads
-  (QKV of layer 0 reads the previous token's LMHEAD: wait_prev_token = 1);
-  LMHEAD's layer field is L.  Unused slots are zero.
+  ``a, b`` = row range (row-tiled stages), as above for ATTN and AREDUCE;
+  ``wait_stage`` is the stage whose outputs the instruction reads (QKV of
+  layer 0 reads the previous token's LMHEAD: wait_prev_token = 1); LMHEAD's
+  layer field is L.  Unused slots are zero.
 
 Parity pins: tests check the validator invariants (every row of every stage
 produced exactly once, waits name the producing stage and its size, lists in
@@ -47,14 +48,15 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 MAGIC = 0x314B444D
-VERSION = 2
+VERSION = 3
 WORDS = 16
 
 OP_QKV, OP_ATTN, OP_AREDUCE, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD = range(1, 10)
 OP_NAMES = {OP_QKV: "QKV", OP_ATTN: "ATTN", OP_AREDUCE: "AREDUCE", OP_OPROJ: "OPROJ",
             OP_UPGATE: "UPGATE", OP_DOWN: "DOWN", OP_MOE_UPGATE: "MOE_UPGATE",
             OP_MOE_DOWN: "MOE_DOWN", OP_LMHEAD: "LMHEAD"}
-GEMV_OPS = (OP_QKV, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD)
+# stages whose instructions are row tiles
+TILED_OPS = (OP_QKV, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD)
 
 
 def stages(cfg, n_chunks: int) -> List[Tuple[int, int, int]]:
@@ -63,7 +65,7 @@ def stages(cfg, n_chunks: int) -> List[Tuple[int, int, int]]:
     qkv_rows = cfg.qd + 2 * cfg.kvd
     for l in range(cfg.n_layers):
         out.append((OP_QKV, l, qkv_rows))
-        out.append((OP_ATTN, l, cfg.n_kv_heads * n_chunks))
+        out.append((OP_ATTN, l, cfg.n_q_heads if n_chunks == 1 else cfg.n_kv_heads * n_chunks))
         if n_chunks > 1:
             out.append((OP_AREDUCE, l, cfg.n_q_heads))
         out.append((OP_OPROJ, l, cfg.d_model))
@@ -90,10 +92,12 @@ def placement(st: List[Tuple[int, int, int]], s: int, n_wg: int) -> Tuple[int, i
 def stage_instructions(op: int, layer: int, size: int, n_wg: int, n_chunks: int) -> List[Tuple[int, int]]:
     """The (a, b) operand pairs of one stage's instructions, by index;
     ``n_wg`` is the number of blocks the stage may use."""
-    if op in GEMV_OPS:
+    if op in TILED_OPS:
         n = min(n_wg, size)
         return [(i * size // n, (i + 1) * size // n) for i in range(n)]
     if op == OP_ATTN:
+        if n_chunks == 1:
+            return [(i, 0) for i in range(size)]
         return [(i // n_chunks, i % n_chunks) for i in range(size)]
     if op == OP_AREDUCE:
         return [(i, 0) for i in range(size)]
@@ -178,7 +182,7 @@ def validate(words: np.ndarray, cfg) -> None:
             raise ValueError(f"stage {s}: instruction indices")
         if [(x[1], x[2]) for x in got] != want:
             raise ValueError(f"stage {s}: operands")
-        if op in GEMV_OPS:
+        if op in TILED_OPS:
             rows = np.zeros(sz, dtype=np.int64)
             for _, a, b in got:
                 rows[a:b] += 1
@@ -203,24 +207,24 @@ def chunk_range(T: int, n_chunks: int, c: int) -> Tuple[int, int]:
     return min(T, c * clen), min(T, (c + 1) * clen)
 
 
-def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_lm_tiles: int, t: int, start_pos: int):
+def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_tiles: Dict[str, int], t: int, start_pos: int):
     """Element reads and writes of one instruction at token t.
 
     Buffers hold tagged values; a read of (buffer, element) expects the
     version written at ``(t, layer)`` named in the tuple.  Buffers: 'h'
     (residual entering a layer), 'qkv', 'part' (attention partials),
-    'aout', 'hmid', 'act', 'route', 'lm' (per-tile max/argmax), and 'kv'
-    (cache rows, element = (layer, kv_head, position); version = token that
-    appended it, -1 for the context present before the run).
+    'aout', 'hmid', 'act', 'route' (MoE), 'lm' (per-tile max/argmax), and
+    'kv' (cache rows, element = (layer, kv_head, position); version = token
+    that appended it, -1 for the context present before the run).
     """
     op, l, s, i, a, b = ins[:6]
     d, qd, kvd, hd, G = cfg.d_model, cfg.qd, cfg.kvd, cfg.head_dim, cfg.group
-    reads: List[Tuple[str, int, Tuple[int, int]]] = []
-    writes: List[Tuple[str, int, Tuple[int, int]]] = []
+    reads: List[Tuple[str, object, Tuple[int, int]]] = []
+    writes: List[Tuple[str, object, Tuple[int, int]]] = []
 
     def token_reads():
         if t > 0:
-            for k in range(n_lm_tiles):
+            for k in range(n_tiles["lm"]):
                 reads.append(("lm", k, (t - 1, cfg.n_layers)))
 
     if op == OP_QKV:
@@ -230,23 +234,28 @@ def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_lm_tiles: int, t: int, st
             reads.extend(("h", r, (t, l)) for r in range(d))
         writes.extend(("qkv", r, (t, l)) for r in range(a, b))
     elif op == OP_ATTN:
-        kvh, c = a, b
         pos = start_pos + t
+        if n_chunks == 1:
+            qheads, kvh, c = [a], a // G, 0
+            appends = a % G == 0
+        else:
+            qheads, kvh, c = list(range(a * G, (a + 1) * G)), a, b
+            appends = True
         lo, hi = chunk_range(pos + 1, n_chunks, c)
         for j in range(lo, hi):
             if j < pos:
                 reads.append(("kv", (l, kvh, j), (j - start_pos if j >= start_pos else -1, 0)))
-        if lo <= pos < hi:
+        if appends and lo <= pos < hi:
             writes.append(("kv", (l, kvh, pos), (t, 0)))
-        rows = list(range(kvh * G * hd, (kvh + 1) * G * hd))
+        rows = [r for qh in qheads for r in range(qh * hd, (qh + 1) * hd)]
         rows += list(range(qd + kvh * hd, qd + (kvh + 1) * hd))
         rows += list(range(qd + kvd + kvh * hd, qd + kvd + (kvh + 1) * hd))
         reads.extend(("qkv", r, (t, l)) for r in rows)
         if n_chunks > 1:
-            for j in range(kvh * G, (kvh + 1) * G):
+            for j in qheads:
                 writes.append(("part", j * n_chunks + c, (t, l)))
         else:
-            writes.extend(("aout", r, (t, l)) for r in range(kvh * G * hd, (kvh + 1) * G * hd))
+            writes.extend(("aout", r, (t, l)) for r in range(a * hd, (a + 1) * hd))
     elif op == OP_AREDUCE:
         j = a
         reads.extend(("part", j * n_chunks + c, (t, l)) for c in range(n_chunks))
@@ -285,7 +294,7 @@ def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos
     """
     hdr, lists = parse(words)
     n_wg, n_chunks = hdr[2], hdr[5]
-    n_lm = min(n_wg, cfg.vocab)
+    n_tiles = {"lm": min(n_wg, cfg.vocab)}
     rng = random.Random(seed)
     mem: Dict[Tuple[str, object], Tuple[int, int]] = {}
     for l in range(cfg.n_layers):
@@ -302,7 +311,7 @@ def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos
     for w in range(n_wg):
         sw = []
         for t, ins in progs[w]:
-            r, wr = _rw_sets(cfg, ins, n_chunks, n_lm, t, start_pos)
+            r, wr = _rw_sets(cfg, ins, n_chunks, n_tiles, t, start_pos)
             sw.append((r, wr))
             for (buf, e, v) in r:
                 need[(buf, e, v)] = need.get((buf, e, v), 0) + 1

@@ -63,11 +63,13 @@ class MkdError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmkd.so (raises if it has not been built)."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmkd.so (raises if it has not been built).  MKD_LIBRARY names
+    another build of the library to load instead of the in-tree one."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MKD_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m persistent_megakernel_decode_02_amd.build`")

@@ -238,7 +238,7 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
   int best = 4;
   for (int i = 0; i < n_st; ++i) {
     const StageDesc& s = st[i];
-    if (!is_gemv(s.op)) continue;
+    if (!is_tiled(s.op)) continue;
     int avail = n_wg, first = 0;
     placement(st, i, n_wg, &avail, &first);
     const int n = s.size < avail ? s.size : avail;

@@ -10,15 +10,14 @@
 
 namespace mkd {
 
-// ---------------------------------------------------------------- schedule spec v2
+// ---------------------------------------------------------------- schedule spec v3
 constexpr int32_t kMagic = 0x314B444D;
-constexpr int32_t kVersion = 2;
+constexpr int32_t kVersion = 3;
 constexpr int kWords = 16;  // words per header and per instruction
-
 enum Opcode : int32_t {
   OP_NOP = 0,
   OP_QKV = 1,         // RMSNorm + [Wq;Wk;Wv] rows (layer 0 also selects the token and embeds it)
-  OP_ATTN = 2,        // RoPE + KV append + split-KV attention partial of one (kv head, chunk)
+  OP_ATTN = 2,        // RoPE + KV append + attention of one q head (one chunk), or of one (kv head, chunk)
   OP_AREDUCE = 3,     // log-sum-exp merge of one q head's chunk partials
   OP_OPROJ = 4,       // Wo rows + residual
   OP_UPGATE = 5,      // RMSNorm + gate/up rows + SiLU product
@@ -27,7 +26,6 @@ enum Opcode : int32_t {
   OP_MOE_DOWN = 8,    // both routed experts' Wd rows, gate-weighted, + residual
   OP_LMHEAD = 9,      // final RMSNorm + LM-head rows, per-tile (max, argmax)
 };
-
 // instruction word indices
 enum : int { I_OP = 0, I_LAYER, I_STAGE, I_INDEX, I_A, I_B, I_WAIT_STAGE, I_WAIT_COUNT,
              I_WAIT_PREV, I_SIGNAL };
@@ -43,9 +41,9 @@ struct StageDesc {
 int config_check(const mkd_config* c, const char** why);
 void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, int cap);
 int stage_count(const mkd_config* c, int n_chunks);
-// blocks stage s may use, and the first of them (spec v2 placement)
+// blocks stage s may use, and the first of them (spec v3 placement)
 void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, int* first);
-bool is_gemv(int op);
+bool is_tiled(int op);  // stages whose instructions are row tiles
 int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, size_t cap,
                    size_t* n_words, const char** why);
 int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const char** why);

@@ -87,8 +87,14 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 }
 
 __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((GLOBAL const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// LDS words shared by the workgroup's wavefronts.  The explicit address
+// space matters: a volatile access through a generic pointer becomes a flat
+// load, which also counts against the vector-memory counter, so the wait for
+// it would wait for every weight load in flight.
+typedef __attribute__((address_space(3))) volatile int lds_vint;
 __device__ __forceinline__ void ll_store(uint64_t* p, float v, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -150,7 +156,7 @@ struct Ctx {
   float* res;    // residual rows         [d]
   float* out;    // GEMV row results      [out_floats]
   float* red;    // reduction scratch     [kRed]
-  volatile int* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
+  lds_vint* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
   int wg, instr, t, tid, lane, wave;
   int stage, index, wait_stage, wait_count, wait_prev;  // from the instruction words
   uint64_t* tr;                                  // this instruction's trace entry, or null
@@ -158,7 +164,7 @@ struct Ctx {
 
 // Record a device error: the first raiser records where; with stop_all every
 // other workgroup's waits end too.
-__device__ __forceinline__ void raise_at(int32_t* status, volatile int* sflag, int code, bool stop_all,
+__device__ __forceinline__ void raise_at(int32_t* status, lds_vint* sflag, int code, bool stop_all,
                                          int wg, int instr, int t) {
   int expected = 0;
   if (__hip_atomic_compare_exchange_strong(&status[S_CODE], &expected, code, __ATOMIC_RELAXED,
@@ -853,8 +859,11 @@ __device__ __forceinline__ void merge_into(AttnState<G>& s, const float* om, con
   }
 }
 
+// Attention of q heads q0 .. q0 + G - 1 (all of kv head kvh's, or one of
+// them) over one chunk; the instruction may append K/V at pos only when it is
+// the one instruction of its kv head that owns it (may_append).
 template <int HD, int G>
-__device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
+__device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int q0, bool may_append) {
   CKParams& p = c.p;
   constexpr int LPR = HD / 8;     // lanes per K/V row
   constexpr int PPW = 64 / LPR;   // positions per wavefront load
@@ -864,6 +873,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   const int lo = min(T, chunk * clen), hi = min(T, (chunk + 1) * clen);
   const int hic = min(hi, pos);             // cached positions [lo, hic)
   const bool has_new = lo <= pos && pos < hi;
+  const bool append = has_new && may_append;
   const int grp = c.lane / LPR, sub = c.lane % LPR;
 
   const size_t head_elems = (size_t)p.max_seq * HD;
@@ -902,7 +912,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   const int re = c.tid < (G + 1) * (HD / 2) ? c.tid : 0;
   const float cs = ld_f32(p.rope + (size_t)pos * (HD / 2) + re % (HD / 2));
   const float sn = ld_f32(p.rope + (size_t)p.max_seq * (HD / 2) + (size_t)pos * (HD / 2) + re % (HD / 2));
-  const Fetch f[3] = {{p.qkv + kvh * G * HD, G * HD, tag, qs},
+  const Fetch f[3] = {{p.qkv + q0 * HD, G * HD, tag, qs},
                       {p.qkv + p.qd + kvh * HD, HD, tag, ks},
                       {p.qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
   if (!gather_inputs<3>(c, f)) return false;
@@ -929,7 +939,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   __syncthreads();
 
   // append K and V at pos (the chunk holding pos owns it)
-  if (has_new && c.tid < LPR) {
+  if (append && c.tid < LPR) {
     u32x4 kw, vw;
     const float* kk = ks + c.tid * 8;
     const float* vv = vs + c.tid * 8;
@@ -1020,7 +1030,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   // the appended K/V must be visible device-wide before anything that
   // depends on this instruction can run: the storing wavefront waits for its
   // stores to complete before the barrier that precedes the output stores
-  if (has_new && c.wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (append && c.wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // score of the new position (one per head)
   __syncthreads();
   float* pnew = c.red;  // [G] new-position scores
@@ -1053,7 +1063,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
         O = fmaf(vs[i], a, O);
       }
     }
-    const int qh = kvh * G + g;
+    const int qh = q0 + g;
     if (p.n_chunks == 1) {
       ll_store(p.aout + qh * HD + i, O / L, otag);
     } else {
@@ -1069,13 +1079,17 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk) {
   return true;
 }
 
+// One chunk: the instruction is one q head (a), and its kv head's first q
+// head appends.  Several chunks: one (kv head a, chunk b) for all its q heads.
 template <int HD>
-__device__ __forceinline__ bool op_attn_hd(Ctx& c, int l, int kvh, int chunk) {
-  switch (c.p.G) {
-    case 1: return op_attn_t<HD, 1>(c, l, kvh, chunk);
-    case 2: return op_attn_t<HD, 2>(c, l, kvh, chunk);
-    case 3: return op_attn_t<HD, 3>(c, l, kvh, chunk);
-    default: return op_attn_t<HD, 4>(c, l, kvh, chunk);
+__device__ __forceinline__ bool op_attn_hd(Ctx& c, int l, int a, int b) {
+  const int G = c.p.G;
+  if (c.p.n_chunks == 1) return op_attn_t<HD, 1>(c, l, a / G, 0, a, a % G == 0);
+  switch (G) {
+    case 1: return op_attn_t<HD, 1>(c, l, a, b, a, true);
+    case 2: return op_attn_t<HD, 2>(c, l, a, b, a * 2, true);
+    case 3: return op_attn_t<HD, 3>(c, l, a, b, a * 3, true);
+    default: return op_attn_t<HD, 4>(c, l, a, b, a * 4, true);
   }
 }
 
@@ -1113,7 +1127,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
   (void)params;
   CKParams* pk = (CKParams*)__builtin_amdgcn_kernarg_segment_ptr();
   extern __shared__ __align__(16) float smem[];
-  volatile int* sflag = s_flags;
+  lds_vint* sflag = (lds_vint*)s_flags;
   const int wg = blockIdx.x;
   if (threadIdx.x == 0) {
     sflag[0] = 0;

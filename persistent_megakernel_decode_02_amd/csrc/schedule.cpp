@@ -1,14 +1,15 @@
-// Host-side schedule builder and validator (schedule spec v2).
+// Host-side schedule builder and validator (schedule spec v3).
 //
 // The persistent kernel walks a host-built list of every operation of the
 // forward pass (Hyperkernel teardown, "What a megakernel buys"; Kittens VM
 // summary, "Method").  The pages fix no format, tiling or assignment; this
-// file implements this library's spec v2:
+// file implements this library's spec v3:
 //   stages per token: per layer QKV, ATTN, [AREDUCE if n_chunks > 1], OPROJ,
 //   UPGATE|MOE_UPGATE, DOWN|MOE_DOWN; then LMHEAD.
-//   GEMV stage over R rows: n = min(n_wg, R) tiles, tile i = [i*R/n, (i+1)*R/n).
-//   ATTN: hkv * n_chunks instructions (kv_head = i / n_chunks, chunk = i % n_chunks).
-//   AREDUCE: hq instructions.  Instruction i of a stage runs on block
+//   Row-tiled stage over R rows: n = min(n_wg, R) tiles, tile i = [i*R/n, (i+1)*R/n).
+//   ATTN: one chunk -> hq instructions (one q head each); n_chunks > 1 ->
+//   hkv * n_chunks (kv_head = i / n_chunks, chunk = i % n_chunks), merged by
+//   AREDUCE (hq instructions).  Instruction i of a stage runs on block
 //   (offset + i) % n_wg; the offset is 0 except for OPROJ, whose tiles skip
 //   the blocks that ran the stage before it (ATTN, or AREDUCE) when there
 //   are more blocks than that stage has instructions: those blocks finish
@@ -21,7 +22,7 @@
 
 namespace mkd {
 
-bool is_gemv(int op) {
+bool is_tiled(int op) {
   return op == OP_QKV || op == OP_OPROJ || op == OP_UPGATE || op == OP_DOWN ||
          op == OP_MOE_UPGATE || op == OP_MOE_DOWN || op == OP_LMHEAD;
 }
@@ -64,7 +65,7 @@ void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, i
   const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
   for (int l = 0; l < c->n_layers; ++l) {
     push(OP_QKV, l, qd + 2 * kvd);
-    push(OP_ATTN, l, c->n_kv_heads * n_chunks);
+    push(OP_ATTN, l, n_chunks == 1 ? c->n_q_heads : c->n_kv_heads * n_chunks);
     if (n_chunks > 1) push(OP_AREDUCE, l, c->n_q_heads);
     push(OP_OPROJ, l, c->d_model);
     if (c->n_experts) {
@@ -80,7 +81,7 @@ void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, i
 }
 
 static int stage_ninstr(const StageDesc& s, int n_wg) {
-  if (is_gemv(s.op)) return s.size < n_wg ? s.size : n_wg;
+  if (is_tiled(s.op)) return s.size < n_wg ? s.size : n_wg;
   return s.size;
 }
 
@@ -98,13 +99,13 @@ void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, in
 }
 
 static void operands(const StageDesc& s, int n_wg, int n_chunks, int i, int32_t* a, int32_t* b) {
-  if (is_gemv(s.op)) {
+  if (is_tiled(s.op)) {
     const int64_t n = stage_ninstr(s, n_wg), R = s.size;
     *a = (int32_t)(i * R / n);
     *b = (int32_t)((i + 1) * R / n);
   } else if (s.op == OP_ATTN) {
-    *a = i / n_chunks;
-    *b = i % n_chunks;
+    *a = n_chunks == 1 ? i : i / n_chunks;   // q head, or kv head
+    *b = n_chunks == 1 ? 0 : i % n_chunks;   // chunk
   } else {  // AREDUCE
     *a = i;
     *b = 0;
