@@ -5,14 +5,15 @@ from __future__ import annotations
 def chunks_for(head_bytes: int, n_wg: int, n_kv_heads: int) -> int:
     """Split-KV chunk count for ``head_bytes`` of K plus V per KV head.
 
-    Measured on the Llama-1B shape (µs/token, 1 / 2 / 4 / 8 / 16 / 32 chunks):
-    KV 128: 856 / 1086 / 951 / 958 / 963; KV 1024: 1303 / 1356 / 1089 / 1089 / 994;
-    KV 4096: 1912 / 1579 / 1205 / 1193 / 1024; KV 16384: 8 -> 1390, 16 -> 1219,
-    32 -> 1092.  A split costs one more dependency stage (the reduction), which
-    only pays once a head's K/V no longer streams quickly through one workgroup.
+    With one chunk the attention instructions are one per q head (schedule
+    spec v3); with several, one per (kv head, chunk) plus a reduction stage.
+    Measured on the Llama-1B shape (µs/token):
+    KV 128: 1 chunk 811; KV 1024: 1 -> 862, 4 -> 1138, 16 -> 978;
+    KV 4096: 1 -> 1174, 2 -> 1427, 4 -> 1316, 8 -> 1225, 16 -> 988, 32 -> 993;
+    KV 16384: 1 -> 1970, 4 -> 2155, 8 -> 1469, 16 -> 1176, 32 -> 1081.
     The same rule is coded in mkd_build_schedule for n_chunks == 0."""
     cap = max(1, min(64, n_wg // n_kv_heads))
-    if head_bytes <= 128 * 1024:
+    if head_bytes <= 512 * 1024:
         return 1
     if head_bytes <= 2 * 1024 * 1024:
         return min(16, cap)
