@@ -183,60 +183,105 @@ __device__ __forceinline__ void raise_error(Ctx& c, int code, bool stop_all) {
   raise_at(c.p.status, c.sflag, code, stop_all, c.wg, c.instr, c.t);
 }
 
-// Stage n tagged values src[0..n) into dst (LDS).  Each thread issues its
-// loads first, then spins only on the words that were not yet tagged for this
-// step, polling with backoff until they are, the launch is aborted (stop word,
-// another workgroup's error) or the watchdog deadline passes.  No barrier:
-// callers end a batch of fetches with sync_ok().
-__device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
-  for (int base = 0; base < n; base += kThreads * 4) {
-    uint64_t v[4];
+// Staging tagged words into LDS.  A fetch reads the 16-byte aligned span
+// that covers src[0..n) -- every activation buffer is a whole number of
+// 128-byte lines, so the span stays inside it -- two tagged words per
+// 16-byte load, S loads per thread in flight per batch (loads past the span
+// read zeros: the descriptor covers exactly the span).  Words whose tag is
+// still old are then polled one by one, with backoff, until they are
+// current, the launch is aborted (stop word, another workgroup's error) or
+// the watchdog deadline passes.  No barrier: callers end with sync_ok().
+struct Span {
+  const uint64_t* w0;  // first word of the aligned span
+  int lead;            // words of the span before src (0 or 1)
+  int npairs;          // 16-byte loads covering the span
+};
+
+__device__ __forceinline__ Span span_of(const uint64_t* src, int n) {
+  Span sp;
+  const uintptr_t s0 = (uintptr_t)src & ~(uintptr_t)15;
+  sp.w0 = (const uint64_t*)s0;
+  sp.lead = (int)(((uintptr_t)src - s0) >> 3);
+  sp.npairs = n > 0 ? (sp.lead + n + 1) >> 1 : 0;
+  return sp;
+}
+
+template <int S>
+struct Staged {
+  u32x4 v[S];
+};
+
+template <int S>
+__device__ __forceinline__ void ll_issue(Ctx& c, const Span& sp, int base, Staged<S>& st) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(sp.w0, (uint32_t)sp.npairs * 16u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * kThreads + c.tid;
-      if (i < n) v[u] = ll_load(src + i);
+  for (int k = 0; k < S; ++k)
+    st.v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (base + k * kThreads + c.tid) * 16, 0, kSC1);
+}
+
+template <int S>
+__device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, const Staged<S>& st, int n,
+                                          uint32_t tag, float* dst) {
+  unsigned pending = 0;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int i0 = 2 * (base + k * kThreads + c.tid) - sp.lead;
+    if (i0 >= 0 && i0 < n) {
+      if (st.v[k].y == tag) dst[i0] = __uint_as_float(st.v[k].x);
+      else pending |= 1u << (2 * k);
     }
-    unsigned pending = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * kThreads + c.tid;
-      if (i < n) {
-        if ((uint32_t)(v[u] >> 32) == tag) dst[i] = __uint_as_float((uint32_t)v[u]);
-        else pending |= 1u << u;
+    if (i0 + 1 >= 0 && i0 + 1 < n) {
+      if (st.v[k].w == tag) dst[i0 + 1] = __uint_as_float(st.v[k].z);
+      else pending |= 2u << (2 * k);
+    }
+  }
+  if (!pending) return;
+  // some producer's store is still in flight: poll those words
+  const uint64_t t0 = wall_clock64();
+  for (int it = 0; pending; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    for (int b = 0; b < 2 * S; ++b) {
+      if (pending & (1u << b)) {
+        const int wi = 2 * (base + (b >> 1) * kThreads + c.tid) + (b & 1);  // word of the span
+        const uint64_t w = ll_load(sp.w0 + wi);
+        if ((uint32_t)(w >> 32) == tag) {
+          dst[wi - sp.lead] = __uint_as_float((uint32_t)w);
+          pending &= ~(1u << b);
+        }
       }
     }
-    if (pending) {
-      const uint64_t t0 = wall_clock64();
-      for (int it = 0; pending; ++it) {
-        __builtin_amdgcn_s_sleep(1);
-        for (int u = 0; u < 4; ++u) {
-          if (pending & (1u << u)) {
-            const int i = base + u * kThreads + c.tid;
-            const uint64_t w = ll_load(src + i);
-            if ((uint32_t)(w >> 32) == tag) {
-              dst[i] = __uint_as_float((uint32_t)w);
-              pending &= ~(1u << u);
-            }
-          }
-        }
-        if (pending && (it & 15) == 15) {
-          if (c.sflag[0] ||
-              __hip_atomic_load(&c.p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            c.sflag[0] = 1;
-            break;
-          }
-          if (__hip_atomic_load(c.p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
-            raise_error(c, MKD_E_ABORTED, true);
-            break;
-          }
-          if (wall_clock64() - t0 > c.p.watchdog_ticks) {
-            raise_error(c, MKD_E_WATCHDOG, true);
-            break;
-          }
-        }
+    if (pending && (it & 15) == 15) {
+      if (c.sflag[0] ||
+          __hip_atomic_load(&c.p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        c.sflag[0] = 1;
+        break;
+      }
+      if (__hip_atomic_load(c.p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+        raise_error(c, MKD_E_ABORTED, true);
+        break;
+      }
+      if (wall_clock64() - t0 > c.p.watchdog_ticks) {
+        raise_error(c, MKD_E_WATCHDOG, true);
+        break;
       }
     }
   }
+}
+
+// batches of one fetch from pair `from` on, S loads per thread each
+template <int S>
+__device__ __forceinline__ void ll_fetch_from(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst,
+                                              int from) {
+  const Span sp = span_of(src, n);
+  for (int base = from; base < sp.npairs; base += S * kThreads) {
+    Staged<S> st;
+    ll_issue<S>(c, sp, base, st);
+    ll_finish<S>(c, sp, base, st, n, tag, dst);
+  }
+}
+
+__device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
+  ll_fetch_from<8>(c, src, n, tag, dst, 0);
 }
 
 // workgroup barrier; false when the launch is being aborted
@@ -346,11 +391,34 @@ struct Fetch {
 // on any whose store is still in flight.  Reading the vectors before the
 // counter completes would mostly read them twice: in this schedule a
 // workgroup nearly always reaches a stage before its producers finish.
+// The first batch of up to three fetches is issued before any is checked, so
+// one round trip covers an instruction's inputs (8192 words of the first,
+// 2048 of the others); longer inputs take further batches.
 template <int K>
 __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count) {
+  constexpr int S0 = 8, S1 = 2;
   if (!wait_counter(c, stage, step_plus1, count)) return false;
+  Staged<S0> st0;
+  Staged<S1> st1, st2;
+  const Span sp0 = span_of(f[0].src, f[0].n);
+  ll_issue<S0>(c, sp0, 0, st0);
+  Span sp1{}, sp2{};
+  if (K > 1) {
+    sp1 = span_of(f[1].src, f[1].n);
+    ll_issue<S1>(c, sp1, 0, st1);
+  }
+  if (K > 2) {
+    sp2 = span_of(f[2].src, f[2].n);
+    ll_issue<S1>(c, sp2, 0, st2);
+  }
+  ll_finish<S0>(c, sp0, 0, st0, f[0].n, f[0].tag, f[0].dst);
+  if (K > 1) ll_finish<S1>(c, sp1, 0, st1, f[1].n, f[1].tag, f[1].dst);
+  if (K > 2) ll_finish<S1>(c, sp2, 0, st2, f[2].n, f[2].tag, f[2].dst);
+  ll_fetch_from<S0>(c, f[0].src, f[0].n, f[0].tag, f[0].dst, S0 * kThreads);
+  if (K > 1) ll_fetch_from<S1>(c, f[1].src, f[1].n, f[1].tag, f[1].dst, S1 * kThreads);
+  if (K > 2) ll_fetch_from<S1>(c, f[2].src, f[2].n, f[2].tag, f[2].dst, S1 * kThreads);
 #pragma unroll
-  for (int j = 0; j < K; ++j) ll_fetch(c, f[j].src, f[j].n, f[j].tag, f[j].dst);
+  for (int j = 3; j < K; ++j) ll_fetch(c, f[j].src, f[j].n, f[j].tag, f[j].dst);
   if (!sync_ok(c)) return false;
   mark_ready(c);
   return true;
