@@ -103,8 +103,13 @@ MIXTRAL = ModelConfig("mixtral-8x7b-shaped", n_layers=32, d_model=4096,
                       n_q_heads=32, n_kv_heads=8, head_dim=128, d_ff=14336,
                       vocab=32000, n_experts=8, top_k=2, rope_theta=1e6)
 
+# a small top-2 MoE of the Mixtral kind, for parity runs of the MoE opcodes
+TINY_MOE = ModelConfig("tiny-moe", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
+                       head_dim=64, d_ff=512, vocab=1024, n_experts=8, top_k=2, rope_theta=1e6)
+
 PRESETS: Dict[str, ModelConfig] = {
     "tiny": TINY, "llama1b": LLAMA_1B, "llama3b": LLAMA_3B, "mixtral": MIXTRAL,
+    "tiny_moe": TINY_MOE,
 }
 
 WORKLOADS: Dict[str, Workload] = {

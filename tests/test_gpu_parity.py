@@ -119,4 +119,83 @@ def test_llama1b_full_size_kv128():
 
 
 def test_llama1b_full_size_kv1024_split():
-    _full_size("llama1b", 1024, 3)
+    _full_size("llama1b", 1024, 3, n_chunks=16)
+
+
+def test_llama1b_full_size_kv1024_one_chunk():
+    _full_size("llama1b", 1024, 2, n_chunks=1)
+
+
+def test_llama3b_full_size_kv128():
+    """head_dim 128, 3 q heads per kv head"""
+    _full_size("llama3b", 128, 3)
+
+
+def test_llama3b_full_size_kv2048_split():
+    _full_size("llama3b", 2048, 2)
+
+
+def test_llama1b_long_context_kv16384():
+    """split-KV at 32 chunks over a 16K-position cache"""
+    _full_size("llama1b", 16384, 2)
+
+
+@pytest.mark.parametrize("n_wg,n_chunks", [(256, 1), (33, 2)])
+def test_tiny_moe_kv_context(n_wg, n_chunks):
+    """MoE opcodes (router, top-2, both experts' down rows in one
+    instruction) on a small top-2 MoE from a random-filled cache."""
+    cfg = synth.PRESETS["tiny_moe"]
+    T0, N = 40, 8
+    w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
+    say(f"tiny-moe n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab, stream=3)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    otoks, ologits, kv_o = oracle_run(cfg, w_cpu, synth.gen_kv_cache(cfg, T0 + N, T0), first, T0, N)
+    check_run("tiny-moe", toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"
+
+
+@pytest.mark.timeout(900)
+def test_mixtral_full_size_kv1024():
+    """Mixtral-shaped (93 GB of bf16 weights on the GPU), 2 steps.  The oracle
+    reads each weight it needs back from the generated device tensors (host
+    memory cannot hold the fp32 copy), converting per use."""
+    cfg = synth.PRESETS["mixtral"]
+    T0, N = 1024, 2
+    require_gpu()
+    say("mixtral: generating 93 GB of weights on the GPU")
+    w_gpu = []
+    for i in range(len(synth.weight_specs(cfg))):
+        w_gpu.append(synth.gen_weights(cfg, device="cuda", only=[i])[i])
+        if i % 32 == 0:
+            torch.cuda.synchronize()
+            say(f"  tensor {i}")
+    kv_gpu = synth.gen_kv_cache(cfg, T0 + N, T0, device="cuda")
+    torch.cuda.synchronize()
+    n_wg, n_chunks = launch_config(cfg, T0, N)
+    say(f"mixtral T0={T0} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    # the generator is bit-identical on both devices (first test), so the
+    # device tensors are the seeded inputs; spot-check one against the host
+    probe = synth.gen_weights(cfg, device="cpu", only=[4])[4]
+    assert torch.equal(probe, w_gpu[4].cpu())
+    say("mixtral: oracle")
+    orc = om.Oracle(cfg, om.Weights(cfg, lambda i: w_gpu[i], cache=False))
+    kv_o = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + N, T0))
+    otoks, ologits = orc.decode(first, T0, N, kv_o)
+    del w_gpu, kv_gpu
+    torch.cuda.empty_cache()
+    check_run("mixtral", toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"
