@@ -19,7 +19,7 @@
 // Weight streaming.  Batch-1 GEMV is one multiply-add per weight, far below
 // the MFMA ridge point, so no matrix cores: each wavefront streams whole rows
 // with coalesced 16-byte (dwordx4) non-temporal loads into a ring of
-// registers, RING loads deep per lane (128 KiB per CU in flight), and issues
+// registers, RING loads deep per lane (64 KiB per CU in flight), and issues
 // an instruction's first RING loads *before* waiting on its inputs, so weight
 // traffic overlaps the dependency wait (epic-kernel README, "Pipelining for
 // B200 bandwidth" and "L2 prefetching overlapped with prior instructions";
@@ -67,7 +67,7 @@ __device__ __forceinline__ void st_f32(float* p, float v) { *(GLOBAL float*)p = 
 __device__ __forceinline__ void st_i32(int32_t* p, int32_t v) { *(GLOBAL int32_t*)p = v; }
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { *(GLOBAL uint64_t*)p = v; }
 
-constexpr int RING = 16;      // 16-byte weight loads in flight per lane (GEMV)
+constexpr int RING = 8;       // 16-byte weight loads in flight per lane (GEMV)
 constexpr int ARING = 4;      // K/V position steps in flight per lane (attention)
 constexpr int kRed = 256;     // LDS floats reserved for reductions
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
@@ -535,11 +535,15 @@ __device__ __forceinline__ int step_token(Ctx& c, bool* ok) {
 
 // Streams the rows of one instruction through a per-wavefront register ring.
 // Row k of this wavefront's stream is m.row(k) (K bf16 values), dotted with
-// xs[m.xoff(k) .. + K); the result goes to the LDS slot m.slot(k).  Every
-// ring refill is issued unconditionally -- slots past the end of the stream
-// read one shared 16-byte word (an L1 hit) -- and nothing else touches
-// global memory inside the loop, so the compiler can wait for exactly the
-// oldest load instead of draining the ring.
+// xs[m.xoff(k) .. + K); the result goes to the LDS slot m.slot(k).  The
+// stream is S units of 1 KiB (one 16-byte load per lane).  Inside a ring pass
+// whose refills are all needed, every refill is issued without a branch and
+// nothing else touches global memory, so the compiler waits for exactly the
+// oldest load instead of draining the ring; the last pass refills nothing.
+// A CU's vector loads complete in issue order, so every load issued ahead of
+// the next instruction's input fetch delays that fetch: the streamer issues
+// no load it does not need, and the ring is only as deep as the bandwidth
+// needs (8 KiB per wavefront, 64 KiB per CU in flight).
 template <class Map>
 struct RowStream {
   const Map& m;
@@ -556,11 +560,9 @@ struct RowStream {
     row = S > 0 ? (const char*)m.row(0) : nullptr;
   }
   // Weights are read with buffer loads whose descriptor spans exactly the
-  // current row (2K bytes): lanes past a ragged row's end, and every slot
-  // past the end of the stream (descriptor of 0 bytes), read zeros without a
-  // memory access.  So every ring refill is issued unconditionally -- the
-  // compiler can wait for exactly the oldest load -- and costs nothing when
-  // there is nothing to read.
+  // current row (2K bytes): lanes past a ragged row's end, and refills past
+  // the end of the stream in the last refilling pass (descriptor of 0 bytes),
+  // read zeros without a memory access.
   __device__ __forceinline__ u32x4 next() {
     const bool live = ps < S;
     const __amdgpu_buffer_rsrc_t r =
@@ -574,9 +576,14 @@ struct RowStream {
     }
     return v;
   }
+  // the first min(S, RING) units, issued before the instruction's inputs are
+  // waited for
   __device__ __forceinline__ void prefetch() {
 #pragma unroll
-    for (int d = 0; d < RING; ++d) ring[d] = next();
+    for (int d = 0; d < RING; ++d) {
+      if (d < S) ring[d] = next();
+      else ring[d] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   // xs must hold finite values (zero) from each row's K up to the next
   // multiple of 512: lanes past a ragged row's end multiply zero weights
@@ -584,33 +591,37 @@ struct RowStream {
     const float* xl = xs + lane * 8;
     int ck = 0, cseg = 0;
     float acc0 = 0.f, acc1 = 0.f;
+    auto eat = [&](const u32x4 w) {
+      const float* xp = xl + m.xoff(ck) + cseg * 512;
+      const f32x4 a = *(const f32x4*)xp;
+      const f32x4 b = *(const f32x4*)(xp + 4);
+      acc0 = fmaf(bf_lo(w.x), a.x, acc0);
+      acc1 = fmaf(bf_hi(w.x), a.y, acc1);
+      acc0 = fmaf(bf_lo(w.y), a.z, acc0);
+      acc1 = fmaf(bf_hi(w.y), a.w, acc1);
+      acc0 = fmaf(bf_lo(w.z), b.x, acc0);
+      acc1 = fmaf(bf_hi(w.z), b.y, acc1);
+      acc0 = fmaf(bf_lo(w.w), b.z, acc0);
+      acc1 = fmaf(bf_hi(w.w), b.w, acc1);
+      if (++cseg == nseg) {
+        out[m.slot(ck)] = wave_sum(acc0 + acc1);
+        acc0 = 0.f;
+        acc1 = 0.f;
+        cseg = 0;
+        ++ck;
+      }
+    };
     for (int s0 = 0; s0 < S; s0 += RING) {
+      if (s0 + RING < S) {
 #pragma unroll
-      for (int d = 0; d < RING; ++d) {
-        if (s0 + d < S) {
-          const float* xp = xl + m.xoff(ck) + cseg * 512;
-          const f32x4 a = *(const f32x4*)xp;
-          const f32x4 b = *(const f32x4*)(xp + 4);
-          const u32x4 w = ring[d];
-          acc0 = fmaf(bf_lo(w.x), a.x, acc0);
-          acc1 = fmaf(bf_hi(w.x), a.y, acc1);
-          acc0 = fmaf(bf_lo(w.y), a.z, acc0);
-          acc1 = fmaf(bf_hi(w.y), a.w, acc1);
-          acc0 = fmaf(bf_lo(w.z), b.x, acc0);
-          acc1 = fmaf(bf_hi(w.z), b.y, acc1);
-          acc0 = fmaf(bf_lo(w.w), b.z, acc0);
-          acc1 = fmaf(bf_hi(w.w), b.w, acc1);
-          if (++cseg == nseg) {
-            // every lane holds the same sum: an unconditional write keeps
-            // the loop free of divergent branches (same value, same address)
-            out[m.slot(ck)] = wave_sum(acc0 + acc1);
-            acc0 = 0.f;
-            acc1 = 0.f;
-            cseg = 0;
-            ++ck;
-          }
+        for (int d = 0; d < RING; ++d) {
+          eat(ring[d]);
+          ring[d] = next();
         }
-        ring[d] = next();
+      } else {
+#pragma unroll
+        for (int d = 0; d < RING; ++d)
+          if (s0 + d < S) eat(ring[d]);
       }
     }
   }
