@@ -6,6 +6,7 @@
 // copies tensors to the addresses the plan names and launches).
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -54,7 +55,7 @@ struct mkd_model {
            *act = nullptr, *route = nullptr, *lm = nullptr, *flags = nullptr;
   int32_t* d_sched = nullptr;
   size_t sched_words = 0, sched_cap = 0;
-  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, n_stages = 0;
+  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, pre_units = 0, n_stages = 0;
   int flag_stride = 0;
   hipEvent_t done = nullptr;
   hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
@@ -249,6 +250,22 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
   return (best + 3) & ~3;
 }
 
+// Dense gate/up weights staged in LDS ahead of the instruction: as many
+// 1 KiB units per wavefront as the LDS left over holds, up to kPreMax
+// (MKD_PRE_UNITS overrides, within the same bounds).  They are loaded while
+// the workgroup waits out the attention phase, when its own load queue is
+// otherwise empty.
+static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max) {
+  if (c->n_experts > 0 || lds_max <= 0 || lds_used >= (size_t)lds_max) return 0;
+  int n = (int)(((size_t)lds_max - lds_used) / ((size_t)kWaves * 1024));
+  if (n > kPreMax) n = kPreMax;
+  if (const char* e = getenv("MKD_PRE_UNITS")) {
+    const int want = atoi(e);
+    if (want >= 0 && want < n) n = want;
+  }
+  return n;
+}
+
 static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm) {
   const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
   const int qd = c->n_q_heads * hd;
@@ -273,6 +290,9 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
     p.x_floats = x_floats_for(&m->cfg, 1, m->n_cu);
     p.out_floats = out_floats_for(&m->cfg, m->n_cu, 1);
     p.d = m->cfg.d_model;
+    int lds_max = 0;
+    hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
+    p.pre_units = pre_units_for(&m->cfg, lds_bytes(p), lds_max);
     int mx = 0;
     const int rc = max_coop_blocks(m->device, lds_bytes(p), &mx);
     if (rc) return fail(rc, "occupancy query failed");
@@ -293,9 +313,10 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   p.x_floats = x_floats;
   p.out_floats = out_floats;
   p.d = c->d_model;
-  const size_t lds = lds_bytes(p);
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
+  p.pre_units = pre_units_for(c, lds_bytes(p), lds_max);
+  const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
                                        std::to_string(lds_max) + " (use more workgroups)");
@@ -359,6 +380,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   m->n_lm = n_lm;
   m->x_floats = x_floats;
   m->out_floats = out_floats;
+  m->pre_units = p.pre_units;
   return MKD_OK;
 }
 
@@ -441,6 +463,7 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   p.G = c->n_q_heads / c->n_kv_heads; p.tied = c->tied; p.lslots = layer_slots(c);
   p.x_floats = m->x_floats;
   p.out_floats = m->out_floats;
+  p.pre_units = m->pre_units;
   p.eps = c->rms_eps;
   const char* why = "";
   const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, &why);

@@ -51,6 +51,7 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
 // ---------------------------------------------------------------- device parameters
 constexpr int kThreads = 512;  // 8 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
+constexpr int kPreMax = 16;   // cap on pre_units
 constexpr int kFlagAlign = 64;   // per-stage flag arrays start on 256-byte boundaries
 constexpr int kTraceWords = 4;   // per instruction: start, inputs ready, end, unused
 
@@ -92,6 +93,8 @@ struct KParams {
   int32_t L, d, hq, hkv, hd, F, V, E, topk, qd, kvd, G, tied, lslots;
   int32_t x_floats;          // LDS floats reserved for the staged input vector
   int32_t out_floats;        // LDS floats for one instruction's GEMV row results
+  int32_t pre_units;         // dense gate/up: 1 KiB weight units per wavefront staged in LDS
+                             // by the instruction before it (0 = none)
   float eps;
 };
 

@@ -550,14 +550,16 @@ struct RowStream {
   const int K, nseg, S;
   const uint32_t lane16;   // this lane's byte offset inside a 1 KiB segment
   const int lane;
+  const int first;         // units 0 .. first-1 are staged in LDS, not streamed here
   int ps, pseg, pk;        // producer cursor (wave-uniform)
   const char* row;         // the producer's current row
   u32x4 ring[RING];
 
-  __device__ __forceinline__ RowStream(const Map& m_, int K_, int nrows, int lane_)
+  __device__ __forceinline__ RowStream(const Map& m_, int K_, int nrows, int lane_, int first_ = 0)
       : m(m_), K(uni(K_)), nseg(uni((K_ + 511) >> 9)), S(uni(nrows * ((K_ + 511) >> 9))),
-        lane16((uint32_t)lane_ * 16u), lane(lane_), ps(0), pseg(0), pk(0) {
-    row = S > 0 ? (const char*)m.row(0) : nullptr;
+        lane16((uint32_t)lane_ * 16u), lane(lane_), first(uni(first_)), ps(first), pseg(first % nseg),
+        pk(first / nseg) {
+    row = ps < S ? (const char*)m.row(pk) : nullptr;
   }
   // Weights are read with buffer loads whose descriptor spans exactly the
   // current row (2K bytes): lanes past a ragged row's end, and refills past
@@ -576,18 +578,19 @@ struct RowStream {
     }
     return v;
   }
-  // the first min(S, RING) units, issued before the instruction's inputs are
-  // waited for
+  // the first min(S - first, RING) streamed units, issued before the
+  // instruction's inputs are waited for
   __device__ __forceinline__ void prefetch() {
 #pragma unroll
     for (int d = 0; d < RING; ++d) {
-      if (d < S) ring[d] = next();
+      if (d < S - first) ring[d] = next();
       else ring[d] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   // xs must hold finite values (zero) from each row's K up to the next
-  // multiple of 512: lanes past a ragged row's end multiply zero weights
-  __device__ __forceinline__ void run(const float* xs, float* out) {
+  // multiple of 512: lanes past a ragged row's end multiply zero weights.
+  // pre holds units 0 .. first-1 (64 lanes x 16 bytes each), already waited for.
+  __device__ __forceinline__ void run(const float* xs, float* out, const u32x4* pre = nullptr) {
     const float* xl = xs + lane * 8;
     int ck = 0, cseg = 0;
     float acc0 = 0.f, acc1 = 0.f;
@@ -611,8 +614,10 @@ struct RowStream {
         ++ck;
       }
     };
-    for (int s0 = 0; s0 < S; s0 += RING) {
-      if (s0 + RING < S) {
+    for (int u = 0; u < first; ++u) eat(pre[u * 64 + lane]);
+    const int R = S - first;
+    for (int s0 = 0; s0 < R; s0 += RING) {
+      if (s0 + RING < R) {
 #pragma unroll
         for (int d = 0; d < RING; ++d) {
           eat(ring[d]);
@@ -621,7 +626,7 @@ struct RowStream {
       } else {
 #pragma unroll
         for (int d = 0; d < RING; ++d)
-          if (s0 + d < S) eat(ring[d]);
+          if (s0 + d < R) eat(ring[d]);
       }
     }
   }
@@ -731,15 +736,66 @@ __device__ __forceinline__ void lmhead_epilogue(Ctx& c, int a, int b, int index)
 // and RMSNorm + LM head: one code path, the opcode only picks matrices,
 // inputs and the epilogue.  Weights for the first RING loads per lane are
 // requested before the inputs are waited for.
-__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
-  CKParams& p = c.p;
-  GemvDesc g;
+__device__ __forceinline__ void desc_init(GemvDesc& g, int a, int w) {
   g.b00 = g.b01 = g.b02 = g.b10 = g.b11 = g.b12 = nullptr;
   g.s1 = g.s2 = kNoSplit;
   g.R = 1;
   g.xoff1 = 0;
   g.a = a;
-  g.w = c.wave;
+  g.w = w;
+}
+
+// dense gate/up rows of layer l: output row r streams gate row r, then up row r
+__device__ __forceinline__ void desc_upgate(CKParams& p, int l, GemvDesc& g) {
+  g.b00 = lptr(p, l, WL_GATE);
+  g.b10 = lptr(p, l, WL_UP);
+  g.R = 2;
+  g.K = p.d;
+}
+
+// units (1 KiB, one 16-byte load per lane) in wavefront w's stream of a tile
+__device__ __forceinline__ int stream_units(const GemvDesc& g, int nrows_tile, int w) {
+  return g.R * wave_rows(nrows_tile, w) * ((g.K + 511) >> 9);
+}
+
+// LDS staging area of this wavefront's gate/up units, after the reduction scratch
+__device__ __forceinline__ u32x4* pre_area(Ctx& c) {
+  return (u32x4*)(c.red + kRed) + (size_t)c.wave * c.p.pre_units * 64;
+}
+
+// Stage the first pre_units units of this wavefront's stream for the dense
+// gate/up tile [a, b) of layer l in LDS: 16-byte loads that write LDS
+// directly (lane i's bytes land at 16 i of the unit's 1 KiB), issued while the
+// workgroup has nothing else in its load queue.  Rows are read through
+// descriptors that span exactly the row, as in the streamer.  The wavefront
+// waits for its staging loads here: it is about to wait microseconds for its
+// next inputs anyway, and while such loads are outstanding the compiler makes
+// every later LDS access wait for all vector memory operations.
+__device__ __forceinline__ void stage_upgate(Ctx& c, int l, int a, int b) {
+  CKParams& p = c.p;
+  GemvDesc g;
+  desc_init(g, a, c.wave);
+  desc_upgate(p, l, g);
+  const GenMap m{g};
+  const int nseg = (g.K + 511) >> 9;
+  const int n = min(stream_units(g, b - a, c.wave), p.pre_units);
+  __attribute__((address_space(3))) char* dst = (__attribute__((address_space(3))) char*)pre_area(c);
+  int k = 0, seg = 0;
+  for (int u = 0; u < n; ++u) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(m.row(k), (uint32_t)g.K * 2u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + u * 1024, 16, c.lane * 16, seg * 1024, 0, kNT);
+    if (++seg == nseg) {
+      seg = 0;
+      ++k;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
+
+__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  GemvDesc g;
+  desc_init(g, a, c.wave);
   const uint16_t* gamma = nullptr;
   const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
   Fetch f[2] = {{p.h, 0, tag, c.xs}, {p.h, 0, tag, c.res}};
@@ -759,7 +815,7 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
       else f[1] = {p.h + a, b - a, tag, c.res};   // published by the previous layer
       break;
     case OP_UPGATE:
-      g.b00 = lptr(p, l, WL_GATE); g.b10 = lptr(p, l, WL_UP); g.R = 2; g.K = p.d;
+      desc_upgate(p, l, g);
       gamma = lptr(p, l, WL_FFN_NORM);
       f[0] = {p.hmid, p.d, tag, c.xs};
       break;
@@ -775,7 +831,10 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
       break;
   }
   const GenMap m{g};
-  RowStream<GenMap> rs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane);
+  // the previous instruction of this workgroup staged a gate/up tile's first
+  // units in LDS (see stage_upgate)
+  const int npre = op == OP_UPGATE && c.instr > 0 ? min(stream_units(g, b - a, c.wave), p.pre_units) : 0;
+  RowStream<GenMap> rs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane, npre);
   rs.prefetch();
   const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
   if (embed_x) {
@@ -793,7 +852,8 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
     __syncthreads();
   }
   if (gamma) rmsnorm_g(c, p.d, gamma, gr);
-  rs.run(c.xs, c.out);
+  // staged units were written by this wavefront, which waited for them
+  rs.run(c.xs, c.out, pre_area(c));
   mark_computed(c);
   __syncthreads();
   switch (op) {
@@ -1236,6 +1296,13 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
             ldc_i32(ins + I_STAGE), index, ldc_i32(ins + I_WAIT_STAGE), ldc_i32(ins + I_WAIT_COUNT),
             ldc_i32(ins + I_WAIT_PREV), tr};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
+      // Dense gate/up weights are staged in LDS by the instruction before
+      // them: at the start of an O-projection (whose wait spans the whole
+      // attention phase), else at the end of the instruction, once its own
+      // loads are done.
+      const int32_t* nx = i + 1 < n ? ins + kWords : nullptr;
+      const bool stage = p.pre_units > 0 && nx && ldc_i32(nx + I_OP) == OP_UPGATE;
+      if (stage && op == OP_OPROJ) stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
       switch (op) {
         case OP_QKV:
         case OP_OPROJ:
@@ -1249,6 +1316,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
         default: break;
       }
       if (ok) signal_done(c);
+      if (ok && stage && op != OP_OPROJ) stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
     }
   }
   // the last step's argmax
@@ -1276,7 +1344,8 @@ extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
 // ---------------------------------------------------------------- host-side launch
 
 size_t lds_bytes(const KParams& p) {
-  return ((size_t)p.x_floats + (size_t)p.d + (size_t)p.out_floats + kRed) * sizeof(float);
+  return ((size_t)p.x_floats + (size_t)p.d + (size_t)p.out_floats + kRed) * sizeof(float) +
+         (size_t)p.pre_units * kWaves * 1024;
 }
 
 int max_coop_blocks(int device, size_t lds, int* out) {
