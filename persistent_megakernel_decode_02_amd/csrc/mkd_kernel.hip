@@ -657,7 +657,7 @@ struct GemvDesc {
 
 struct GenMap {
   const GemvDesc& g;
-  __device__ const uint16_t* row(int k) const {
+  __device__ __forceinline__ const uint16_t* row(int k) const {
     const bool two = g.R == 2;
     const int j = two ? (k >> 1) : k;
     const bool s = two && (k & 1);
@@ -668,8 +668,8 @@ struct GenMap {
     const uint16_t* p1 = psel(in2, psel(in1, g.b10, g.b11), g.b12);
     return psel(s, p0, p1) + (size_t)(r - r0) * g.K;
   }
-  __device__ int xoff(int k) const { return (g.R == 2 && (k & 1)) ? g.xoff1 : 0; }
-  __device__ int slot(int k) const {
+  __device__ __forceinline__ int xoff(int k) const { return (g.R == 2 && (k & 1)) ? g.xoff1 : 0; }
+  __device__ __forceinline__ int slot(int k) const {
     return g.R == 2 ? 2 * (g.w + (k >> 1) * kWaves) + (k & 1) : g.w + k * kWaves;
   }
 };
@@ -753,18 +753,14 @@ __device__ __forceinline__ void desc_upgate(CKParams& p, int l, GemvDesc& g) {
   g.K = p.d;
 }
 
-// units (1 KiB, one 16-byte load per lane) in wavefront w's stream of a tile
-__device__ __forceinline__ int stream_units(const GemvDesc& g, int nrows_tile, int w) {
-  return g.R * wave_rows(nrows_tile, w) * ((g.K + 511) >> 9);
-}
-
 // LDS staging area of this wavefront's gate/up units, after the reduction scratch
 __device__ __forceinline__ u32x4* pre_area(Ctx& c) {
   return (u32x4*)(c.red + kRed) + (size_t)c.wave * c.p.pre_units * 64;
 }
 
-// Stage the first pre_units units of this wavefront's stream for the dense
-// gate/up tile [a, b) of layer l in LDS: 16-byte loads that write LDS
+// Stage the first stream rows of this wavefront for the dense gate/up tile
+// [a, b) of layer l in LDS, as many whole rows as pre_units units (1 KiB,
+// one 16-byte load per lane) hold: 16-byte loads that write LDS
 // directly (lane i's bytes land at 16 i of the unit's 1 KiB), issued while the
 // workgroup has nothing else in its load queue.  Rows are read through
 // descriptors that span exactly the row, as in the streamer.  The wavefront
@@ -778,7 +774,7 @@ __device__ __forceinline__ void stage_upgate(Ctx& c, int l, int a, int b) {
   desc_upgate(p, l, g);
   const GenMap m{g};
   const int nseg = (g.K + 511) >> 9;
-  const int n = min(stream_units(g, b - a, c.wave), p.pre_units);
+  const int n = min(g.R * wave_rows(b - a, c.wave), p.pre_units / nseg) * nseg;   // whole rows
   __attribute__((address_space(3))) char* dst = (__attribute__((address_space(3))) char*)pre_area(c);
   int k = 0, seg = 0;
   for (int u = 0; u < n; ++u) {
@@ -792,14 +788,20 @@ __device__ __forceinline__ void stage_upgate(Ctx& c, int l, int a, int b) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
-__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
+// Matrices, inputs and norm gains of one dense GEMV instruction (the opcode
+// picks them; everything else is shared): the row map g, the tagged inputs
+// f (vector, residual rows), the RMSNorm gains of the vector (or null) and
+// whether the vector (layer 0 QKV) or the residual rows (layer 0 O-proj)
+// come from the embedding instead.
+__device__ __forceinline__ void gemv_setup(Ctx& c, int op, int l, int a, int b, uint32_t tag, GemvDesc& g,
+                                           Fetch (&f)[2], const uint16_t*& gamma, bool& embed_x,
+                                           bool& embed_res) {
   CKParams& p = c.p;
-  GemvDesc g;
   desc_init(g, a, c.wave);
-  const uint16_t* gamma = nullptr;
-  const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
-  Fetch f[2] = {{p.h, 0, tag, c.xs}, {p.h, 0, tag, c.res}};
-  bool embed_x = false, embed_res = false;
+  gamma = nullptr;
+  f[0] = {p.h, 0, tag, c.xs};
+  f[1] = {p.h, 0, tag, c.res};
+  embed_x = embed_res = false;
   switch (op) {
     case OP_QKV:
       g.b00 = lptr(p, l, WL_Q); g.b01 = lptr(p, l, WL_K); g.b02 = lptr(p, l, WL_V);
@@ -830,13 +832,12 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
       f[0] = {p.h, p.d, tag, c.xs};
       break;
   }
-  const GenMap m{g};
-  // the previous instruction of this workgroup staged a gate/up tile's first
-  // units in LDS (see stage_upgate)
-  const int npre = op == OP_UPGATE && c.instr > 0 ? min(stream_units(g, b - a, c.wave), p.pre_units) : 0;
-  RowStream<GenMap> rs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane, npre);
-  rs.prefetch();
-  const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
+}
+
+// stage the instruction's input vector in LDS (xs, and the residual rows in res)
+__device__ __forceinline__ bool gemv_inputs(Ctx& c, int a, int b, int K, const Fetch (&f)[2], bool embed_x,
+                                            bool embed_res) {
+  CKParams& p = c.p;
   if (embed_x) {
     // the token comes from the previous step's LM-head partials (it waits on
     // them itself); the embedding row is a plain read
@@ -847,15 +848,16 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
     if (embed_res && !embed_rows(c, a, b, c.res)) return false;
     if (!gather_inputs<2>(c, f)) return false;
   }
-  if (g.K & 511) {
-    pad_zero(c, c.xs, g.K);
+  if (K & 511) {
+    pad_zero(c, c.xs, K);
     __syncthreads();
   }
-  if (gamma) rmsnorm_g(c, p.d, gamma, gr);
-  // staged units were written by this wavefront, which waited for them
-  rs.run(c.xs, c.out, pre_area(c));
-  mark_computed(c);
-  __syncthreads();
+  return true;
+}
+
+// write the instruction's outputs from the row results in LDS
+__device__ __forceinline__ void gemv_epilogue(Ctx& c, int op, int l, int a, int b, int index, uint32_t tag) {
+  CKParams& p = c.p;
   switch (op) {
     case OP_QKV:
       for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.qkv + a + i, c.out[i], tag);
@@ -876,7 +878,233 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
       lmhead_epilogue(c, a, b, index);
       break;
   }
+}
+
+// stream rows of this wavefront whose weights the previous instruction of
+// the workgroup staged in LDS (gate/up only; see stage_upgate)
+__device__ __forceinline__ int staged_rows(Ctx& c, int op, int ns, int nseg) {
+  return op == OP_UPGATE && c.instr > 0 ? min(ns, c.p.pre_units / nseg) : 0;
+}
+
+// Any row length: rows stream through the runtime-length RowStream, the
+// input vector is read from LDS per 1 KiB unit.
+__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
+  GemvDesc g;
+  Fetch f[2];
+  const uint16_t* gamma;
+  bool embed_x, embed_res;
+  gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
+  const GenMap m{g};
+  const int nseg = (g.K + 511) >> 9;
+  const int ns = g.R * wave_rows(b - a, c.wave);
+  RowStream<GenMap> rs(m, g.K, ns, c.lane, staged_rows(c, op, ns, nseg) * nseg);
+  rs.prefetch();
+  const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
+  if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
+  if (gamma) rmsnorm_g(c, p.d, gamma, gr);
+  // staged units were written by this wavefront, which waited for them
+  rs.run(c.xs, c.out, pre_area(c));
+  mark_computed(c);
+  __syncthreads();
+  gemv_epilogue(c, op, l, a, b, index, tag);
   return true;
+}
+
+// Absolute output row r of part `part` (0, or 1 for the up rows).
+__device__ __forceinline__ const uint16_t* row_of(const GemvDesc& g, int r, int part) {
+  const bool in1 = r >= g.s1, in2 = r >= g.s2;
+  const int r0 = in2 ? g.s2 : (in1 ? g.s1 : 0);
+  const uint16_t* p0 = psel(in2, psel(in1, g.b00, g.b01), g.b02);
+  const uint16_t* p1 = psel(in2, psel(in1, g.b10, g.b11), g.b12);
+  return psel(part != 0, p0, p1) + (size_t)(r - r0) * g.K;
+}
+
+// A wavefront's stream rows in order (output rows r0, r0 + kWaves, ...; with
+// R == 2 each output row streams its gate row, then its up row), stepped by
+// pointer increments except where the Q|K|V split points are crossed.
+struct RowCursor {
+  const GemvDesc& g;
+  int r, part;
+  const uint16_t* p0;
+  const uint16_t* p1;
+  __device__ __forceinline__ RowCursor(const GemvDesc& g_, int r0) : g(g_), r(r0), part(0) {
+    p0 = row_of(g, r, 0);
+    p1 = g.R == 2 ? row_of(g, r, 1) : p0;
+  }
+  __device__ __forceinline__ const uint16_t* next() {
+    const uint16_t* q = part ? p1 : p0;
+    if (g.R == 2 && part == 0) {
+      part = 1;
+      return q;
+    }
+    part = 0;
+    const int nr = r + kWaves;
+    const bool cross = (r < g.s1 && nr >= g.s1) || (r < g.s2 && nr >= g.s2);
+    r = nr;
+    if (cross) {
+      p0 = row_of(g, r, 0);
+      p1 = g.R == 2 ? row_of(g, r, 1) : p0;
+    } else {
+      p0 += (size_t)kWaves * g.K;
+      p1 += (size_t)kWaves * g.K;
+    }
+    return q;
+  }
+};
+
+// Row length NSEG x 512 (rows shorter by less than 512 read zeros past
+// their end).  Each lane keeps its 8-element slices of the input vector for
+// all NSEG segments in registers, so a 1 KiB weight unit costs 16 VALU
+// operations and no LDS traffic, and RMSNorm runs inside each wavefront on
+// those registers (every wavefront holds the whole vector) without a
+// workgroup barrier.  The register ring holds RROWS rows (16 units): the
+// first half is requested before the inputs are waited for, the second
+// half as soon as they have arrived, so HBM keeps streaming while the
+// wavefront normalises and works through the rows already on chip.  Every
+// load after the inputs have arrived is issued without a branch (rows past
+// the end use a zero-size descriptor), which keeps the compiler's waits
+// exact: each row waits only for its own loads.
+template <int NSEG>
+__device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b, int index) {
+  constexpr int RROWS = 16 / NSEG > 1 ? 16 / NSEG : 1;
+  constexpr int HROWS = RROWS / 2 > 1 ? RROWS / 2 : 1;
+  CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
+  GemvDesc g;
+  Fetch f[2];
+  const uint16_t* gamma;
+  bool embed_x, embed_res;
+  gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
+  const int lane = c.lane;
+  const uint32_t rbytes = (uint32_t)g.K * 2u;
+  const int ns = g.R * wave_rows(b - a, c.wave);   // stream rows of this wavefront
+  const int npre = staged_rows(c, op, ns, NSEG);    // ... of which staged in LDS
+  const int nq = ns - npre;                         // ... and streamed through the ring
+  RowCursor cur(g, a + c.wave);
+  for (int i = 0; i < npre; ++i) cur.next();
+
+  u32x4 ring[RROWS][NSEG];
+  auto load_row = [&](u32x4 (&dst)[NSEG], const uint16_t* row, bool live) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, live ? rbytes : 0u);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s)
+      dst[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, s * 1024, kNT);
+  };
+#pragma unroll
+  for (int h = 0; h < HROWS; ++h)
+    if (h < nq) load_row(ring[h], cur.next(), true);
+  // norm gains for this lane's slices (zeros past d)
+  u32x4 gv[NSEG];
+  if (gamma) {
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(gamma, (uint32_t)p.d * 2u);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) gv[s] = __builtin_amdgcn_raw_buffer_load_b128(gr, (s * 512 + lane * 8) * 2, 0, 0);
+  }
+  if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
+  // everything requested so far has arrived (it was issued before the
+  // inputs, and loads complete in order); saying so keeps the waits below exact
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const bool deep = nq > HROWS;
+  if (deep) {
+#pragma unroll
+    for (int h = HROWS; h < RROWS; ++h) load_row(ring[h], cur.next(), h < nq);
+  }
+
+  float x[NSEG][8];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const f32x4 u = *(const f32x4*)(c.xs + s * 512 + lane * 8);
+    const f32x4 v = *(const f32x4*)(c.xs + s * 512 + lane * 8 + 4);
+    x[s][0] = u.x; x[s][1] = u.y; x[s][2] = u.z; x[s][3] = u.w;
+    x[s][4] = v.x; x[s][5] = v.y; x[s][6] = v.z; x[s][7] = v.w;
+  }
+  if (gamma) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(x[s][i], x[s][i], ss);
+    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.d + p.eps);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      const uint32_t gw[4] = {gv[s].x, gv[s].y, gv[s].z, gv[s].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[s][2 * i] = (x[s][2 * i] * inv) * bf_lo(gw[i]);
+        x[s][2 * i + 1] = (x[s][2 * i + 1] * inv) * bf_hi(gw[i]);
+      }
+    }
+  }
+  auto dot_row = [&](const u32x4 (&w)[NSEG]) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      a0 = fmaf(bf_lo(w[s].x), x[s][0], a0);
+      a1 = fmaf(bf_hi(w[s].x), x[s][1], a1);
+      a0 = fmaf(bf_lo(w[s].y), x[s][2], a0);
+      a1 = fmaf(bf_hi(w[s].y), x[s][3], a1);
+      a0 = fmaf(bf_lo(w[s].z), x[s][4], a0);
+      a1 = fmaf(bf_hi(w[s].z), x[s][5], a1);
+      a0 = fmaf(bf_lo(w[s].w), x[s][6], a0);
+      a1 = fmaf(bf_hi(w[s].w), x[s][7], a1);
+    }
+    return wave_sum(a0 + a1);
+  };
+  // LDS slot of stream row k; every lane writes the same value to it
+  const GenMap m{g};
+  // rows staged in LDS (written by this wavefront, which waited for them)
+  const u32x4* pre = pre_area(c);
+  for (int q = 0; q < npre; ++q) {
+    u32x4 w[NSEG];
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) w[s] = pre[(q * NSEG + s) * 64 + lane];
+    c.out[m.slot(q)] = dot_row(w);
+  }
+  if (!deep) {
+#pragma unroll
+    for (int h = 0; h < HROWS; ++h)
+      if (h < nq) c.out[m.slot(npre + h)] = dot_row(ring[h]);
+  } else {
+    int q0 = 0;
+    for (; q0 + 2 * RROWS <= nq; q0 += RROWS) {   // every refill is a live row
+#pragma unroll
+      for (int h = 0; h < RROWS; ++h) {
+        c.out[m.slot(npre + q0 + h)] = dot_row(ring[h]);
+        load_row(ring[h], cur.next(), true);
+      }
+    }
+    if (q0 + RROWS < nq) {                          // last refilling pass
+#pragma unroll
+      for (int h = 0; h < RROWS; ++h) {
+        c.out[m.slot(npre + q0 + h)] = dot_row(ring[h]);
+        load_row(ring[h], cur.next(), q0 + RROWS + h < nq);
+      }
+      q0 += RROWS;
+    }
+#pragma unroll
+    for (int h = 0; h < RROWS; ++h)                 // drain
+      if (q0 + h < nq) c.out[m.slot(npre + q0 + h)] = dot_row(ring[h]);
+  }
+  mark_computed(c);
+  __syncthreads();
+  gemv_epilogue(c, op, l, a, b, index, tag);
+  return true;
+}
+
+// dense GEMV opcodes: the compile-time row length when there is one
+__device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  const int K = op == OP_OPROJ ? p.qd : (op == OP_DOWN ? p.F : p.d);
+  switch ((K + 511) >> 9) {
+    case 1: return op_gemv_fast<1>(c, op, l, a, b, index);
+    case 2: return op_gemv_fast<2>(c, op, l, a, b, index);
+    case 4: return op_gemv_fast<4>(c, op, l, a, b, index);
+    case 6: return op_gemv_fast<6>(c, op, l, a, b, index);
+    case 8: return op_gemv_fast<8>(c, op, l, a, b, index);
+    default: return op_gemv(c, op, l, a, b, index);
+  }
 }
 
 // ---------------------------------------------------------------- opcodes: MoE
@@ -1308,7 +1536,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
         case OP_OPROJ:
         case OP_UPGATE:
         case OP_DOWN:
-        case OP_LMHEAD: ok = op_gemv(c, op, l, a, b, index); break;
+        case OP_LMHEAD: ok = op_gemv_any(c, op, l, a, b, index); break;
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
         case OP_MOE_UPGATE: ok = op_moe_upgate(c, l, a, b, index); break;
