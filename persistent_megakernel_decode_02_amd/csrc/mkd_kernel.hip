@@ -1400,11 +1400,14 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   if (append && c.wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // score of the new position (one per head)
   __syncthreads();
+  // (wavefront g < G takes head g: one product per lane, then a wave sum)
   float* pnew = c.red;  // [G] new-position scores
-  if (has_new && c.tid < G) {
+  if (has_new && c.wave < G) {
     float s = 0.f;
-    for (int i = 0; i < HD; ++i) s = fmaf(qs[c.tid * HD + i], ks[i], s);
-    pnew[c.tid] = s;
+#pragma unroll
+    for (int i = 0; i < HD / 64; ++i) s = fmaf(qs[c.wave * HD + i * 64 + c.lane], ks[i * 64 + c.lane], s);
+    s = wave_sum(s);
+    if (c.lane == 0) pnew[c.wave] = s;
   }
   __syncthreads();
 
