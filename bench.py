@@ -98,6 +98,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--kv", type=int, default=None, help="starting KV length (default: the workload's first)")
     ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="sequences decoded together (all from the same KV length)")
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=384,
@@ -134,17 +136,26 @@ def main() -> int:
     n_wg = args.n_wg or n_wg
     n_chunks = args.n_chunks or n_chunks
 
-    log(f"generating {cfg.name} weights and a {T0}-position KV cache on the GPU")
+    B = args.batch
+    log(f"generating {cfg.name} weights and {B} {T0}-position KV cache(s) on the GPU")
     w = synth.gen_weights(cfg, device="cuda")
-    kv = synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")
+    if B == 1:
+        kv = synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")
+    else:
+        kv = torch.stack([synth.gen_kv_cache(cfg, max_seq, T0, seed=synth.SEED_KV + 101 * b, device="cuda")
+                          for b in range(B)]).contiguous()
     torch.cuda.synchronize()
-    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks)
-    log(f"schedule: n_wg={dec.n_wg} n_chunks={dec.n_chunks} max_instr={dec.max_instr}")
-    first = synth.gen_tokens(1, cfg.vocab)[0]
-    toks = torch.empty(N, dtype=torch.int32, device="cuda")
+    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B)
+    log(f"schedule: n_wg={dec.n_wg} n_chunks={dec.n_chunks} max_instr={dec.max_instr} batch={B}")
+    firsts = synth.gen_tokens(B, cfg.vocab)
+    first = firsts[0]
+    toks = torch.empty(B, N, dtype=torch.int32, device="cuda")
 
     def one():
-        dec.launch(first, T0, N, toks)
+        if B == 1:
+            dec.launch(first, T0, N, toks)
+        else:
+            dec.launch_batch(firsts, [T0] * B, N, toks)
         capi.mkd_wait(dec.handle, 600000)
         return capi.mkd_kernel_ms(dec.handle)
 
@@ -163,23 +174,23 @@ def main() -> int:
 
     ms_per_step = wall * 1e3 / args.steps
     kernel_s = float(np.mean(kms)) / 1e3
-    n_bytes = roofline.run_bytes(cfg, T0, N)
+    n_bytes = roofline.run_bytes(cfg, T0, N) if B == 1 else roofline.batch_run_bytes(cfg, [T0] * B, N)
     achieved = n_bytes / kernel_s
     peak = roofline.HBM_PEAK_BYTES_PER_S
     floor_us = roofline.floor_seconds(n_bytes) * 1e6 / N
 
-    if args.trace:
+    if args.trace and B == 1:
         trace_breakdown(dec, first, T0, N)
 
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(cfg, T0, args.cpu_sample, first)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
-    key = f"{args.workload}_kv{T0}_n{N}"
+    key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
     traffic = measured_traffic(key)
     out = {
-        "metric": "batch-1 decode tokens/s",
-        "value": N * args.steps / wall,
+        "metric": "batch-1 decode tokens/s" if B == 1 else f"batch-{B} decode tokens/s",
+        "value": B * N * args.steps / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -190,16 +201,17 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name} decoder, batch 1, KV cache {T0} positions, {N} greedy "
+        "config": {"workload": f"{cfg.name} decoder, batch {B}, KV cache {T0} positions, {N} greedy "
                                f"decode steps per step (one launch)",
                    "weights": "bf16", "kv_cache": "bf16", "activations": "fp32",
                    "kv_start": T0, "decode_tokens_per_step": N, "n_wg": dec.n_wg,
                    "n_chunks": dec.n_chunks, "parallelism": "single GPU"},
-        "us_per_token": kernel_s * 1e6 / N,
+        "us_per_token": kernel_s * 1e6 / N,   # per decode step (all sequences)
         "roofline_us_per_token": floor_us,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "mkd_megakernel", "algorithmic_bytes_per_launch": n_bytes,
+                     "kernel": "mkd_megakernel" if B == 1 else "mkd_megakernel_batch",
+                     "algorithmic_bytes_per_launch": n_bytes,
                      "kernel_ms_mean": kernel_s * 1e3},
         "cpu_baseline": cpu,
     }

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MKD_ABI_VERSION 1
+#define MKD_ABI_VERSION 2
 
 enum {
   MKD_OK = 0,
@@ -110,8 +110,8 @@ int mkd_weight_shape(const mkd_config* cfg, size_t index, int64_t* rows, int64_t
  * bf16 [n_layers][2 (K, V)][n_kv_heads][max_seq][head_dim]. */
 int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out);
 
-/* Build the instruction tensor (schedule spec v2) on the host, without a
- * device.  The spec -- stage order, GEMV row tiling, round-robin block
+/* Build the instruction tensor (schedule spec v4, one sequence) on the host,
+ * without a device.  The spec -- stage order, GEMV row tiling, round-robin block
  * assignment (O-projection tiles skip the blocks that ran attention or its
  * reduction), word layout -- is this library's own; the pages fix none of it
  * (they only say the blocks follow a host-built schedule of every operation,
@@ -121,6 +121,15 @@ int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out
  * *n_words receives the size.  MKD_E_INVALID if capacity is too small. */
 int mkd_schedule_build(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks,
                        int32_t* out, size_t capacity, size_t* n_words);
+
+/* As mkd_schedule_build, for `batch` sequences decoded together (1..8): the
+ * row-tiled instructions compute their rows for every sequence, attention and
+ * its reduction are repeated per sequence (word 10 names it), and header word
+ * 15 records the batch.  Each weight is then read once per step for all
+ * sequences.  No page describes a batched megakernel; the Kittens VM summary
+ * ("Results") quotes a decode figure of a related kernel at a 4-prompt batch. */
+int mkd_schedule_build_batch(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch,
+                             int32_t* out, size_t capacity, size_t* n_words);
 
 /* Check a schedule tensor's invariants (ranges, every row of every stage
  * produced exactly once, waits naming the producing stage, lists in stage
@@ -138,6 +147,15 @@ int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_
  * cooperative launch). */
 int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights,
              void* kv_cache, int32_t max_seq, int32_t device, mkd_model** out);
+
+/* As mkd_init, for `batch` sequences (1..8) decoded together by
+ * mkd_decode_batch.  kv_cache holds `batch` caches one after the other:
+ * batch * mkd_kv_cache_bytes(cfg, max_seq) bytes, sequence b's cache at byte
+ * b * mkd_kv_cache_bytes(cfg, max_seq).  Dense models only for batch > 1
+ * (MKD_E_UNSUPPORTED for MoE: each sequence would route to its own experts).
+ * Schedules built or loaded for the handle must have the same batch. */
+int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights,
+                   void* kv_cache, int32_t max_seq, int32_t batch, int32_t device, mkd_model** out);
 
 /* Query the device's compute-unit count and the largest grid a cooperative
  * launch of the megakernel can hold on it. */
@@ -170,6 +188,17 @@ int mkd_load_schedule(mkd_model* m, const int32_t* words, size_t n_words);
 int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_steps,
                const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev,
                void* stream);
+
+/* Enqueue ONE cooperative launch that decodes n_steps tokens for each of the
+ * handle's `batch` sequences together (mkd_init_batch).  Sequence b starts
+ * from first_tokens[b] at position start_pos[b] (host arrays of `batch`
+ * entries) and proceeds greedily as in mkd_decode; every step reads each
+ * weight once for all sequences.
+ * tokens_out_dev: device int32[batch][n_steps].
+ * logits_out_dev: device float[batch][n_steps][vocab] or NULL.
+ * Asynchronous; errors as mkd_decode. */
+int mkd_decode_batch(mkd_model* m, const int32_t* first_tokens, const int32_t* start_pos, int32_t n_steps,
+                     int32_t* tokens_out_dev, float* logits_out_dev, void* stream);
 
 /* Wait up to timeout_ms (< 0: forever) for the last mkd_decode and read the
  * device status (out may be NULL).  The device-side watchdog (mkd_set_watchdog)

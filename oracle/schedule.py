@@ -5,11 +5,15 @@ each block reads a host-built instruction tensor to decide its next work
 (Kittens VM summary, "Method"); the blocks get "a schedule of every operation
 in the forward pass" and synchronise on the device (Hyperkernel teardown,
 "What a megakernel buys").  The pages fix no format, tiling or assignment, so
-the tensor below is this project's own specification ("schedule spec v3",
+the tensor below is this project's own specification ("schedule spec v4",
 also written out in the design notes); the GPU library's C++ builder must
 produce the same bytes.
 
-Spec v3 (all int32):
+Spec v4 (all int32):
+
+* a launch decodes B sequences together (batch B >= 1): every row-tiled
+  instruction computes its rows for all B, attention and its reduction are
+  per sequence.
 
 * stage order per token: for each layer ``QKV, ATTN, [AREDUCE if n_chunks > 1],
   OPROJ, UPGATE|MOE_UPGATE, DOWN|MOE_DOWN``; then ``LMHEAD``.
@@ -19,6 +23,9 @@ Spec v3 (all int32):
 * ATTN: with one chunk, one instruction per q head (a = q head, b = 0); with
   several, one per (kv head, chunk) serving the kv head's q heads together
   (a = kv head, b = chunk), and AREDUCE has hq (a = q head) merging them.
+  Each of these is repeated for every sequence: instruction i of the stage
+  serves sequence ``i // n`` (n = instructions per sequence) with the operands
+  of instruction ``i % n`` above, and names the sequence in word 10.
 * instruction i of a stage goes to block ``(offset + i) % n_wg``; a block's
   list is the concatenation of its instructions in stage order.  The offset
   is 0 except for OPROJ: its tiles skip the blocks that ran the stage just
@@ -27,9 +34,9 @@ Spec v3 (all int32):
   blocks than that, OPROJ has ``min(d, n_wg - E)`` tiles at offset E, E being
   the preceding stage's instruction count.
 * words: header[16] = {magic, version, n_wg, n_stages, max_instr, n_chunks, L,
-  d, hq, hkv, hd, F, V, E, top_k, total_instr}; counts[n_wg]; then
+  d, hq, hkv, hd, F, V, E, top_k, B}; counts[n_wg]; then
   ``[n_wg][max_instr][16]`` with instruction = {opcode, layer, stage, index,
-  a, b, wait_stage, wait_count, wait_prev_token, signal_stage, 0...};
+  a, b, wait_stage, wait_count, wait_prev_token, signal_stage, sequence, 0...};
   ``a, b`` = row range (row-tiled stages), as above for ATTN and AREDUCE;
   ``wait_stage`` is the stage whose outputs the instruction reads (QKV of
   layer 0 reads the previous token's LMHEAD: wait_prev_token = 1); LMHEAD's
@@ -48,7 +55,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 MAGIC = 0x314B444D
-VERSION = 3
+VERSION = 4
 WORDS = 16
 
 OP_QKV, OP_ATTN, OP_AREDUCE, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD = range(1, 10)
@@ -59,15 +66,15 @@ OP_NAMES = {OP_QKV: "QKV", OP_ATTN: "ATTN", OP_AREDUCE: "AREDUCE", OP_OPROJ: "OP
 TILED_OPS = (OP_QKV, OP_OPROJ, OP_UPGATE, OP_DOWN, OP_MOE_UPGATE, OP_MOE_DOWN, OP_LMHEAD)
 
 
-def stages(cfg, n_chunks: int) -> List[Tuple[int, int, int]]:
+def stages(cfg, n_chunks: int, batch: int = 1) -> List[Tuple[int, int, int]]:
     """(opcode, layer, rows-or-count) for every stage of one token, in order."""
     out = []
     qkv_rows = cfg.qd + 2 * cfg.kvd
     for l in range(cfg.n_layers):
         out.append((OP_QKV, l, qkv_rows))
-        out.append((OP_ATTN, l, cfg.n_q_heads if n_chunks == 1 else cfg.n_kv_heads * n_chunks))
+        out.append((OP_ATTN, l, batch * (cfg.n_q_heads if n_chunks == 1 else cfg.n_kv_heads * n_chunks)))
         if n_chunks > 1:
-            out.append((OP_AREDUCE, l, cfg.n_q_heads))
+            out.append((OP_AREDUCE, l, batch * cfg.n_q_heads))
         out.append((OP_OPROJ, l, cfg.d_model))
         if cfg.is_moe:
             out.append((OP_MOE_UPGATE, l, cfg.top_k * cfg.d_ff))
@@ -89,30 +96,33 @@ def placement(st: List[Tuple[int, int, int]], s: int, n_wg: int) -> Tuple[int, i
     return n_wg, 0
 
 
-def stage_instructions(op: int, layer: int, size: int, n_wg: int, n_chunks: int) -> List[Tuple[int, int]]:
-    """The (a, b) operand pairs of one stage's instructions, by index;
+def stage_instructions(op: int, layer: int, size: int, n_wg: int, n_chunks: int,
+                       batch: int = 1) -> List[Tuple[int, int, int]]:
+    """The (a, b, sequence) operands of one stage's instructions, by index;
     ``n_wg`` is the number of blocks the stage may use."""
     if op in TILED_OPS:
         n = min(n_wg, size)
-        return [(i * size // n, (i + 1) * size // n) for i in range(n)]
+        return [(i * size // n, (i + 1) * size // n, 0) for i in range(n)]
+    per = size // batch
     if op == OP_ATTN:
         if n_chunks == 1:
-            return [(i, 0) for i in range(size)]
-        return [(i // n_chunks, i % n_chunks) for i in range(size)]
+            return [(i % per, 0, i // per) for i in range(size)]
+        return [((i % per) // n_chunks, (i % per) % n_chunks, i // per) for i in range(size)]
     if op == OP_AREDUCE:
-        return [(i, 0) for i in range(size)]
+        return [(i % per, 0, i // per) for i in range(size)]
     raise ValueError(op)
 
 
-def build(cfg, n_wg: int, n_chunks: int) -> np.ndarray:
-    """Instruction tensor (int32 words) for ``cfg`` on ``n_wg`` blocks."""
-    if n_wg < 1 or n_chunks < 1:
-        raise ValueError("n_wg and n_chunks must be >= 1")
-    st = stages(cfg, n_chunks)
+def build(cfg, n_wg: int, n_chunks: int, batch: int = 1) -> np.ndarray:
+    """Instruction tensor (int32 words) for ``cfg`` on ``n_wg`` blocks,
+    decoding ``batch`` sequences together."""
+    if n_wg < 1 or n_chunks < 1 or batch < 1:
+        raise ValueError("n_wg, n_chunks and batch must be >= 1")
+    st = stages(cfg, n_chunks, batch)
     n_st = len(st)
     lists: List[List[List[int]]] = [[] for _ in range(n_wg)]
     places = [placement(st, s, n_wg) for s in range(n_st)]
-    counts_per_stage = [len(stage_instructions(op, l, sz, places[s][0], n_chunks))
+    counts_per_stage = [len(stage_instructions(op, l, sz, places[s][0], n_chunks, batch))
                         for s, (op, l, sz) in enumerate(st)]
     for s, (op, l, sz) in enumerate(st):
         if s == 0:
@@ -120,15 +130,14 @@ def build(cfg, n_wg: int, n_chunks: int) -> np.ndarray:
         else:
             wait_stage, wait_prev = s - 1, 0
         avail, first = places[s]
-        for i, (a, b) in enumerate(stage_instructions(op, l, sz, avail, n_chunks)):
-            words = [op, l, s, i, a, b, wait_stage, counts_per_stage[wait_stage], wait_prev, s]
+        for i, (a, b, seq) in enumerate(stage_instructions(op, l, sz, avail, n_chunks, batch)):
+            words = [op, l, s, i, a, b, wait_stage, counts_per_stage[wait_stage], wait_prev, s, seq]
             words += [0] * (WORDS - len(words))
             lists[(first + i) % n_wg].append(words)
     max_instr = max(len(x) for x in lists)
-    total = sum(len(x) for x in lists)
     hdr = [MAGIC, VERSION, n_wg, n_st, max_instr, n_chunks, cfg.n_layers, cfg.d_model,
            cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ff, cfg.vocab,
-           cfg.n_experts, cfg.top_k, total]
+           cfg.n_experts, cfg.top_k, batch]
     body = np.zeros((n_wg, max_instr, WORDS), dtype=np.int32)
     for w, lst in enumerate(lists):
         if lst:
@@ -152,15 +161,19 @@ def validate(words: np.ndarray, cfg) -> None:
     hdr, lists = parse(words)
     if hdr[0] != MAGIC or hdr[1] != VERSION:
         raise ValueError("bad magic/version")
-    n_wg, n_st, max_instr, n_chunks = hdr[2], hdr[3], hdr[4], hdr[5]
-    st = stages(cfg, n_chunks)
+    n_wg, n_st, max_instr, n_chunks, batch = hdr[2], hdr[3], hdr[4], hdr[5], hdr[15]
+    if batch < 1:
+        raise ValueError("batch")
+    st = stages(cfg, n_chunks, batch)
     if n_st != len(st):
         raise ValueError("stage count")
-    seen: Dict[int, List[Tuple[int, int]]] = {s: [] for s in range(n_st)}
+    seen: Dict[int, List[Tuple[int, int, int, int]]] = {s: [] for s in range(n_st)}
     for w, lst in enumerate(lists):
         prev = -1
         for ins in lst:
-            op, l, s, i, a, b, ws, wc, wp, sig = ins[:10]
+            op, l, s, i, a, b, ws, wc, wp, sig, seq = ins[:11]
+            if any(ins[11:]):
+                raise ValueError("reserved words")
             if not (0 <= s < n_st) or st[s][0] != op or st[s][1] != l:
                 raise ValueError(f"wg {w}: stage/opcode mismatch {ins}")
             if s < prev:
@@ -174,17 +187,17 @@ def validate(words: np.ndarray, cfg) -> None:
             want_ws = n_st - 1 if s == 0 else s - 1
             if ws != want_ws or wp != (1 if s == 0 else 0):
                 raise ValueError("wait stage")
-            seen[s].append((i, a, b))
+            seen[s].append((i, a, b, seq))
     for s, (op, l, sz) in enumerate(st):
         got = sorted(seen[s])
-        want = stage_instructions(op, l, sz, placement(st, s, n_wg)[0], n_chunks)
+        want = stage_instructions(op, l, sz, placement(st, s, n_wg)[0], n_chunks, batch)
         if [x[0] for x in got] != list(range(len(want))):
             raise ValueError(f"stage {s}: instruction indices")
-        if [(x[1], x[2]) for x in got] != want:
+        if [(x[1], x[2], x[3]) for x in got] != want:
             raise ValueError(f"stage {s}: operands")
         if op in TILED_OPS:
             rows = np.zeros(sz, dtype=np.int64)
-            for _, a, b in got:
+            for _, a, b, _ in got:
                 rows[a:b] += 1
             if not np.all(rows == 1):
                 raise ValueError(f"stage {s}: rows not covered exactly once")
@@ -207,34 +220,40 @@ def chunk_range(T: int, n_chunks: int, c: int) -> Tuple[int, int]:
     return min(T, c * clen), min(T, (c + 1) * clen)
 
 
-def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_tiles: Dict[str, int], t: int, start_pos: int):
+def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_tiles: Dict[str, int], t: int,
+             start_pos: Sequence[int], batch: int):
     """Element reads and writes of one instruction at token t.
 
     Buffers hold tagged values; a read of (buffer, element) expects the
     version written at ``(t, layer)`` named in the tuple.  Buffers: 'h'
     (residual entering a layer), 'qkv', 'part' (attention partials),
     'aout', 'hmid', 'act', 'route' (MoE), 'lm' (per-tile max/argmax), and
-    'kv' (cache rows, element = (layer, kv_head, position); version = token
-    that appended it, -1 for the context present before the run).
+    'kv' (cache rows, element = (sequence, layer, kv_head, position); version =
+    token that appended it, -1 for the context present before the run).
+    Every element but the cache's carries its sequence first.
     """
     op, l, s, i, a, b = ins[:6]
+    seq = ins[10]
     d, qd, kvd, hd, G = cfg.d_model, cfg.qd, cfg.kvd, cfg.head_dim, cfg.group
     reads: List[Tuple[str, object, Tuple[int, int]]] = []
     writes: List[Tuple[str, object, Tuple[int, int]]] = []
+    seqs = range(batch)
 
     def token_reads():
         if t > 0:
-            for k in range(n_tiles["lm"]):
-                reads.append(("lm", k, (t - 1, cfg.n_layers)))
+            for q in seqs:
+                for k in range(n_tiles["lm"]):
+                    reads.append(("lm", (q, k), (t - 1, cfg.n_layers)))
 
     if op == OP_QKV:
         if l == 0:
             token_reads()
         else:
-            reads.extend(("h", r, (t, l)) for r in range(d))
-        writes.extend(("qkv", r, (t, l)) for r in range(a, b))
+            reads.extend(("h", (q, r), (t, l)) for q in seqs for r in range(d))
+        writes.extend(("qkv", (q, r), (t, l)) for q in seqs for r in range(a, b))
     elif op == OP_ATTN:
-        pos = start_pos + t
+        p0 = start_pos[seq]
+        pos = p0 + t
         if n_chunks == 1:
             qheads, kvh, c = [a], a // G, 0
             appends = a % G == 0
@@ -244,63 +263,68 @@ def _rw_sets(cfg, ins: Sequence[int], n_chunks: int, n_tiles: Dict[str, int], t:
         lo, hi = chunk_range(pos + 1, n_chunks, c)
         for j in range(lo, hi):
             if j < pos:
-                reads.append(("kv", (l, kvh, j), (j - start_pos if j >= start_pos else -1, 0)))
+                reads.append(("kv", (seq, l, kvh, j), (j - p0 if j >= p0 else -1, 0)))
         if appends and lo <= pos < hi:
-            writes.append(("kv", (l, kvh, pos), (t, 0)))
+            writes.append(("kv", (seq, l, kvh, pos), (t, 0)))
         rows = [r for qh in qheads for r in range(qh * hd, (qh + 1) * hd)]
         rows += list(range(qd + kvh * hd, qd + (kvh + 1) * hd))
         rows += list(range(qd + kvd + kvh * hd, qd + kvd + (kvh + 1) * hd))
-        reads.extend(("qkv", r, (t, l)) for r in rows)
+        reads.extend(("qkv", (seq, r), (t, l)) for r in rows)
         if n_chunks > 1:
             for j in qheads:
-                writes.append(("part", j * n_chunks + c, (t, l)))
+                writes.append(("part", (seq, j * n_chunks + c), (t, l)))
         else:
-            writes.extend(("aout", r, (t, l)) for r in range(a * hd, (a + 1) * hd))
+            writes.extend(("aout", (seq, r), (t, l)) for r in range(a * hd, (a + 1) * hd))
     elif op == OP_AREDUCE:
         j = a
-        reads.extend(("part", j * n_chunks + c, (t, l)) for c in range(n_chunks))
-        writes.extend(("aout", r, (t, l)) for r in range(j * hd, (j + 1) * hd))
+        reads.extend(("part", (seq, j * n_chunks + c), (t, l)) for c in range(n_chunks))
+        writes.extend(("aout", (seq, r), (t, l)) for r in range(j * hd, (j + 1) * hd))
     elif op == OP_OPROJ:
-        reads.extend(("aout", r, (t, l)) for r in range(qd))
+        reads.extend(("aout", (q, r), (t, l)) for q in seqs for r in range(qd))
         if l == 0:
             token_reads()
         else:
-            reads.extend(("h", r, (t, l)) for r in range(a, b))
-        writes.extend(("hmid", r, (t, l)) for r in range(a, b))
+            reads.extend(("h", (q, r), (t, l)) for q in seqs for r in range(a, b))
+        writes.extend(("hmid", (q, r), (t, l)) for q in seqs for r in range(a, b))
     elif op in (OP_UPGATE, OP_MOE_UPGATE):
-        reads.extend(("hmid", r, (t, l)) for r in range(d))
-        writes.extend(("act", r, (t, l)) for r in range(a, b))
+        reads.extend(("hmid", (q, r), (t, l)) for q in seqs for r in range(d))
+        writes.extend(("act", (q, r), (t, l)) for q in seqs for r in range(a, b))
         if op == OP_MOE_UPGATE and i == 0:
-            writes.append(("route", 0, (t, l)))
+            writes.extend(("route", (q, 0), (t, l)) for q in seqs)
     elif op in (OP_DOWN, OP_MOE_DOWN):
         n_act = cfg.d_ff * (cfg.top_k if op == OP_MOE_DOWN else 1)
-        reads.extend(("act", r, (t, l)) for r in range(n_act))
+        reads.extend(("act", (q, r), (t, l)) for q in seqs for r in range(n_act))
         if op == OP_MOE_DOWN:
-            reads.append(("route", 0, (t, l)))
-        reads.extend(("hmid", r, (t, l)) for r in range(a, b))
-        writes.extend(("h", r, (t, l + 1)) for r in range(a, b))
+            reads.extend(("route", (q, 0), (t, l)) for q in seqs)
+        reads.extend(("hmid", (q, r), (t, l)) for q in seqs for r in range(a, b))
+        writes.extend(("h", (q, r), (t, l + 1)) for q in seqs for r in range(a, b))
     elif op == OP_LMHEAD:
-        reads.extend(("h", r, (t, l)) for r in range(d))
-        writes.append(("lm", i, (t, l)))
+        reads.extend(("h", (q, r), (t, l)) for q in seqs for r in range(d))
+        writes.extend(("lm", (q, i), (t, l)) for q in seqs)
     return reads, writes
 
 
-def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos: int = 0) -> None:
+def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos=0) -> None:
     """Run every block's list under a random interleaving of tagged buffers.
 
-    An instruction may run when every element it reads holds the version it
+    ``start_pos``: one position for every sequence, or one per sequence.  An
+    instruction may run when every element it reads holds the version it
     expects.  Raises on deadlock (no block can run) and on a write that would
     replace a version some pending instruction still has to read.
     """
     hdr, lists = parse(words)
-    n_wg, n_chunks = hdr[2], hdr[5]
+    n_wg, n_chunks, batch = hdr[2], hdr[5], hdr[15]
+    starts = [int(start_pos)] * batch if np.isscalar(start_pos) else [int(x) for x in start_pos]
+    if len(starts) != batch:
+        raise ValueError("one start position per sequence")
     n_tiles = {"lm": min(n_wg, cfg.vocab)}
     rng = random.Random(seed)
     mem: Dict[Tuple[str, object], Tuple[int, int]] = {}
-    for l in range(cfg.n_layers):
-        for h in range(cfg.n_kv_heads):
-            for j in range(start_pos):
-                mem[("kv", (l, h, j))] = (-1, 0)
+    for q in range(batch):
+        for l in range(cfg.n_layers):
+            for h in range(cfg.n_kv_heads):
+                for j in range(starts[q]):
+                    mem[("kv", (q, l, h, j))] = (-1, 0)
     # every (token, block, position) as a job in program order
     progs = [[(t, ins) for t in range(n_tokens) for ins in lst] for lst in lists]
     pc = [0] * n_wg
@@ -311,7 +335,7 @@ def simulate(cfg, words: np.ndarray, n_tokens: int = 2, seed: int = 0, start_pos
     for w in range(n_wg):
         sw = []
         for t, ins in progs[w]:
-            r, wr = _rw_sets(cfg, ins, n_chunks, n_tiles, t, start_pos)
+            r, wr = _rw_sets(cfg, ins, n_chunks, n_tiles, t, starts, batch)
             sw.append((r, wr))
             for (buf, e, v) in r:
                 need[(buf, e, v)] = need.get((buf, e, v), 0) + 1

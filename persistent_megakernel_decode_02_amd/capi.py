@@ -34,8 +34,9 @@ OPCODE_NAMES = {1: "QKV", 2: "ATTN", 3: "AREDUCE", 4: "OPROJ", 5: "UPGATE", 6: "
 # every function include/mkd.h declares
 EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_count",
            "mkd_weight_shape", "mkd_kv_cache_bytes", "mkd_schedule_build",
-           "mkd_schedule_validate", "mkd_init", "mkd_device_info", "mkd_build_schedule",
-           "mkd_load_schedule", "mkd_decode", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
+           "mkd_schedule_build_batch", "mkd_schedule_validate", "mkd_init", "mkd_init_batch",
+           "mkd_device_info", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
+           "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
            "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_destroy")
 
 
@@ -84,12 +85,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_weight_shape": ([cfgp, SZ, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
         "mkd_kv_cache_bytes": ([cfgp, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_schedule_build": ([cfgp, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
+        "mkd_schedule_build_batch": ([cfgp, I32, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_schedule_validate": ([cfgp, P, SZ], ctypes.c_int),
         "mkd_init": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
+        "mkd_init_batch": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
         "mkd_device_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_build_schedule": ([P, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_load_schedule": ([P, P, SZ], ctypes.c_int),
         "mkd_decode": ([P, I32, I32, I32, P, P, P, P], ctypes.c_int),
+        "mkd_decode_batch": ([P, P, P, I32, P, P, P], ctypes.c_int),
         "mkd_wait": ([P, I32, ctypes.POINTER(mkd_status)], ctypes.c_int),
         "mkd_abort": ([P], ctypes.c_int),
         "mkd_set_watchdog": ([P, I32], ctypes.c_int),
@@ -165,6 +169,16 @@ def mkd_schedule_build(cfg: mkd_config, n_wg: int, n_chunks: int) -> np.ndarray:
     return out
 
 
+def mkd_schedule_build_batch(cfg: mkd_config, n_wg: int, n_chunks: int, batch: int) -> np.ndarray:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.mkd_schedule_build_batch(ctypes.byref(cfg), n_wg, n_chunks, batch, None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=np.int32)
+    _check(lib.mkd_schedule_build_batch(ctypes.byref(cfg), n_wg, n_chunks, batch, out.ctypes.data, out.size,
+                                        ctypes.byref(n)))
+    return out
+
+
 def mkd_schedule_validate(cfg: mkd_config, words: np.ndarray) -> None:
     w = np.ascontiguousarray(words, dtype=np.int32)
     _check(load().mkd_schedule_validate(ctypes.byref(cfg), w.ctypes.data, w.size))
@@ -176,6 +190,16 @@ def mkd_init(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, device:
     h = ctypes.c_void_p()
     _check(load().mkd_init(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, device,
                            ctypes.byref(h)))
+    return h.value
+
+
+def mkd_init_batch(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, batch: int,
+                   device: int = 0) -> int:
+    """As mkd_init for ``batch`` sequences; ``kv_cache`` holds every sequence's cache."""
+    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    h = ctypes.c_void_p()
+    _check(load().mkd_init_batch(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, batch,
+                                 device, ctypes.byref(h)))
     return h.value
 
 
@@ -210,6 +234,18 @@ def mkd_decode(m: int, first_token: int, start_pos: int, n_steps: int, tokens_ou
         stream = torch.cuda.current_stream().cuda_stream
     _check(load().mkd_decode(m, first_token, start_pos, n_steps, _ptr(forced), _ptr(tokens_out),
                              _ptr(logits_out), stream))
+
+
+def mkd_decode_batch(m: int, first_tokens: Sequence[int], start_pos: Sequence[int], n_steps: int,
+                     tokens_out, logits_out=None, stream=None) -> None:
+    """Enqueue one launch for every sequence of a batched handle (host lists in,
+    device tensors out: tokens [B, n_steps] int32, logits [B, n_steps, V] float32)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    ft = (ctypes.c_int32 * len(first_tokens))(*[int(x) for x in first_tokens])
+    sp = (ctypes.c_int32 * len(start_pos))(*[int(x) for x in start_pos])
+    _check(load().mkd_decode_batch(m, ft, sp, n_steps, _ptr(tokens_out), _ptr(logits_out), stream))
 
 
 def mkd_wait(m: int, timeout_ms: int = -1, raise_on_error: bool = True) -> mkd_status:

@@ -55,7 +55,10 @@ struct mkd_model {
            *act = nullptr, *route = nullptr, *lm = nullptr, *flags = nullptr;
   int32_t* d_sched = nullptr;
   size_t sched_words = 0, sched_cap = 0;
-  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, pre_units = 0, n_stages = 0;
+  int batch = 1;  // sequences decoded together
+  int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, res_floats = 0;
+  int pre_units = 0, n_stages = 0;
+  int32_t s_qkv = 0, s_part = 0;  // per-sequence strides of qkv and part (words)
   int flag_stride = 0;
   hipEvent_t done = nullptr;
   hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
@@ -128,12 +131,17 @@ int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out
   return MKD_OK;
 }
 
-int mkd_schedule_build(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t* out,
-                       size_t capacity, size_t* n_words) {
+int mkd_schedule_build_batch(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch,
+                             int32_t* out, size_t capacity, size_t* n_words) {
   const char* why = "";
-  const int rc = schedule_build(cfg, n_wg, n_chunks, out, capacity, n_words, &why);
+  const int rc = schedule_build(cfg, n_wg, n_chunks, batch, out, capacity, n_words, &why);
   if (rc) return fail(rc, why);
   return MKD_OK;
+}
+
+int mkd_schedule_build(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t* out,
+                       size_t capacity, size_t* n_words) {
+  return mkd_schedule_build_batch(cfg, n_wg, n_chunks, 1, out, capacity, n_words);
 }
 
 int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_words) {
@@ -145,8 +153,16 @@ int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_
 
 int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
              int32_t max_seq, int32_t device, mkd_model** out) {
+  return mkd_init_batch(cfg, weights, n_weights, kv_cache, max_seq, 1, device, out);
+}
+
+int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
+                   int32_t max_seq, int32_t batch, int32_t device, mkd_model** out) {
   if (!out) return fail(MKD_E_INVALID, "null out");
   *out = nullptr;
+  if (batch < 1 || batch > kMaxBatch) return fail(MKD_E_INVALID, "batch must be in [1, 8]");
+  if (batch > 1 && cfg && cfg->n_experts)
+    return fail(MKD_E_UNSUPPORTED, "batched decode is implemented for dense models only");
   size_t want = 0;
   int rc = mkd_weight_count(cfg, &want);
   if (rc) return rc;
@@ -175,6 +191,7 @@ int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights
 
   mkd_model* m = new mkd_model();
   m->cfg = *cfg;
+  m->batch = batch;
   m->device = device;
   m->n_cu = prop.multiProcessorCount;
   m->max_seq = max_seq;
@@ -230,12 +247,12 @@ int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights
 }
 
 // LDS floats for the GEMV row results of the largest tile (x2 for the
-// opcodes that stream two rows per output row)
-static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
+// opcodes that stream two rows per output row), for every sequence
+static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks, int batch) {
   const int n_st = stage_count(c, n_chunks);
   std::vector<StageDesc> st(n_st);
   int got = 0;
-  stage_list(c, n_chunks, st.data(), &got, n_st);
+  stage_list(c, n_chunks, batch, st.data(), &got, n_st);
   int best = 4;
   for (int i = 0; i < n_st; ++i) {
     const StageDesc& s = st[i];
@@ -247,7 +264,28 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks) {
     if (s.op == OP_UPGATE || s.op == OP_MOE_UPGATE || s.op == OP_MOE_DOWN) rows *= 2;
     best = rows > best ? rows : best;
   }
-  return (best + 3) & ~3;
+  return ((best * batch) + 3) & ~3;
+}
+
+// LDS floats for the residual rows of a tile: the whole vector (as before)
+// with one sequence, the largest O-projection or down tile for each of several
+static int res_floats_for(const mkd_config* c, int n_wg, int n_chunks, int batch) {
+  if (batch == 1) return (c->d_model + 3) & ~3;
+  const int n_st = stage_count(c, n_chunks);
+  std::vector<StageDesc> st(n_st);
+  int got = 0;
+  stage_list(c, n_chunks, batch, st.data(), &got, n_st);
+  int best = 4;
+  for (int i = 0; i < n_st; ++i) {
+    const StageDesc& s = st[i];
+    if (s.op != OP_OPROJ && s.op != OP_DOWN && s.op != OP_MOE_DOWN) continue;
+    int avail = n_wg, first = 0;
+    placement(st, i, n_wg, &avail, &first);
+    const int n = s.size < avail ? s.size : avail;
+    const int rows = (s.size + n - 1) / n;
+    best = rows > best ? rows : best;
+  }
+  return ((best + 3) & ~3) * batch;
 }
 
 // Dense gate/up weights staged in LDS ahead of the instruction: as many
@@ -266,7 +304,9 @@ static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max) {
   return n;
 }
 
-static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm) {
+static int32_t round16i(int64_t n) { return (int32_t)((n + 15) / 16 * 16); }
+
+static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch) {
   const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
   const int qd = c->n_q_heads * hd;
   auto pad = [](int n) { return (n + 511) & ~511; };   // streamer rows read x in 512-wide segments
@@ -274,7 +314,9 @@ static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm) {
   x = x > pad(qd) ? x : pad(qd);
   const int act = pad(c->d_ff) * (c->top_k ? c->top_k : 1);
   x = x > act ? x : act;
-  x = x > 2 * n_lm ? x : 2 * n_lm;
+  x *= batch;                                           // one input vector per sequence
+  const int lm = 2 * n_lm * batch;                      // every sequence's LM-head partials
+  x = x > lm ? x : lm;
   const int ared = n_chunks * (hd + 2);
   x = x > ared ? x : ared;
   const int attn = (G + 2) * hd + kWaves * G * (hd + 2);
@@ -287,14 +329,16 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
   if (n_cu) *n_cu = m->n_cu;
   if (max_coop_wg) {
     KParams p{};
-    p.x_floats = x_floats_for(&m->cfg, 1, m->n_cu);
-    p.out_floats = out_floats_for(&m->cfg, m->n_cu, 1);
+    const int n_lm = m->cfg.vocab < m->n_cu ? m->cfg.vocab : m->n_cu;
+    p.x_floats = x_floats_for(&m->cfg, 1, n_lm, m->batch);
+    p.out_floats = out_floats_for(&m->cfg, m->n_cu, 1, m->batch);
+    p.res_floats = res_floats_for(&m->cfg, m->n_cu, 1, m->batch);
     p.d = m->cfg.d_model;
     int lds_max = 0;
     hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
-    p.pre_units = pre_units_for(&m->cfg, lds_bytes(p), lds_max);
+    p.pre_units = m->batch == 1 ? pre_units_for(&m->cfg, lds_bytes(p), lds_max) : 0;
     int mx = 0;
-    const int rc = max_coop_blocks(m->device, lds_bytes(p), &mx);
+    const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, &mx);
     if (rc) return fail(rc, "occupancy query failed");
     *max_coop_wg = mx;
   }
@@ -303,25 +347,30 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
 
 static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   const mkd_config* c = &m->cfg;
-  const int n_wg = words[H_NWG], n_chunks = words[H_NCHUNKS];
+  const int n_wg = words[H_NWG], n_chunks = words[H_NCHUNKS], batch = words[H_BATCH];
   if (n_chunks > 64) return fail(MKD_E_UNSUPPORTED, "n_chunks > 64 is not supported by the device code");
   if (n_wg > 4096) return fail(MKD_E_UNSUPPORTED, "n_wg > 4096 is not supported by the device code");
+  if (batch != m->batch)
+    return fail(MKD_E_INVALID, "schedule is for " + std::to_string(batch) + " sequences, the model decodes " +
+                                   std::to_string(m->batch));
   const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
-  const int x_floats = x_floats_for(c, n_chunks, n_lm);
-  const int out_floats = out_floats_for(c, n_wg, n_chunks);
+  const int x_floats = x_floats_for(c, n_chunks, n_lm, batch);
+  const int out_floats = out_floats_for(c, n_wg, n_chunks, batch);
+  const int res_floats = res_floats_for(c, n_wg, n_chunks, batch);
   KParams p{};
   p.x_floats = x_floats;
   p.out_floats = out_floats;
+  p.res_floats = res_floats;
   p.d = c->d_model;
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
-  p.pre_units = pre_units_for(c, lds_bytes(p), lds_max);
+  p.pre_units = batch == 1 ? pre_units_for(c, lds_bytes(p), lds_max) : 0;
   const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
                                        std::to_string(lds_max) + " (use more workgroups)");
   int mx = 0;
-  int rc = max_coop_blocks(m->device, lds, &mx);
+  int rc = max_coop_blocks(m->device, lds, batch, &mx);
   if (rc) return fail(rc, "occupancy query failed");
   if (n_wg > mx)
     return fail(MKD_E_COOPERATIVE, "n_wg " + std::to_string(n_wg) + " exceeds the " +
@@ -352,12 +401,17 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
       }
     for (int v : per) flag_stride = std::max(flag_stride, (v + kFlagAlign - 1) / kFlagAlign * kFlagAlign);
   }
-  // tagged activation buffers, one allocation (cleared before each launch)
+  // tagged activation buffers, one allocation (cleared before each launch):
+  // h, aout, hmid, act and lm interleave the sequences (element r of sequence
+  // b at r * batch + b); qkv and part hold one block per sequence, 128-byte
+  // aligned
   const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
-  const size_t sz[9] = {round16(c->d_model), round16(qd + 2 * kvd),
-                        round16((size_t)c->n_q_heads * n_chunks * (c->head_dim + 2)), round16(qd),
-                        round16(c->d_model), round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1)),
-                        16, round16(2 * (size_t)n_lm),
+  const int32_t s_qkv = round16i(qd + 2 * kvd),
+                s_part = round16i((int64_t)c->n_q_heads * n_chunks * (c->head_dim + 2));
+  const size_t sz[9] = {round16((size_t)c->d_model * batch), (size_t)batch * s_qkv, (size_t)batch * s_part,
+                        round16((size_t)qd * batch), round16((size_t)c->d_model * batch),
+                        round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1) * batch),
+                        16, round16(2 * (size_t)n_lm * batch),
                         round16((size_t)words[H_NSTAGES] * flag_stride / 2)};
   size_t total = 0;
   for (size_t s : sz) total += s;
@@ -380,7 +434,9 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   m->n_lm = n_lm;
   m->x_floats = x_floats;
   m->out_floats = out_floats;
+  m->res_floats = res_floats;
   m->pre_units = p.pre_units;
+  m->s_qkv = s_qkv; m->s_part = s_part;
   return MKD_OK;
 }
 
@@ -410,10 +466,10 @@ int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks, int32_t* ho
       n_chunks = cap;
   }
   size_t n = 0;
-  int rc = mkd_schedule_build(&m->cfg, n_wg, n_chunks, nullptr, 0, &n);
+  int rc = mkd_schedule_build_batch(&m->cfg, n_wg, n_chunks, m->batch, nullptr, 0, &n);
   if (rc) return rc;
   std::vector<int32_t> w(n);
-  rc = mkd_schedule_build(&m->cfg, n_wg, n_chunks, w.data(), n, &n);
+  rc = mkd_schedule_build_batch(&m->cfg, n_wg, n_chunks, m->batch, w.data(), n, &n);
   if (rc) return rc;
   if (n_words) *n_words = n;
   if (host_out) {
@@ -423,14 +479,18 @@ int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks, int32_t* ho
   return upload_schedule(m, w.data(), n);
 }
 
-int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_steps,
-               const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev, void* stream) {
-  if (!m) return fail(MKD_E_INVALID, "null model");
+// one launch of n_steps decode steps for every sequence of the model
+static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_t* start_pos, int32_t n_steps,
+                         const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev,
+                         void* stream) {
   if (!m->d_sched) return fail(MKD_E_INVALID, "no schedule loaded");
   const mkd_config* c = &m->cfg;
-  if (first_token < 0 || first_token >= c->vocab) return fail(MKD_E_INVALID, "first_token out of range");
-  if (start_pos < 0 || n_steps < 1 || (int64_t)start_pos + n_steps > m->max_seq)
-    return fail(MKD_E_INVALID, "need start_pos >= 0, n_steps >= 1, start_pos + n_steps <= max_seq");
+  if (!first_tokens || !start_pos) return fail(MKD_E_INVALID, "null first_tokens or start_pos");
+  for (int b = 0; b < m->batch; ++b) {
+    if (first_tokens[b] < 0 || first_tokens[b] >= c->vocab) return fail(MKD_E_INVALID, "first token out of range");
+    if (start_pos[b] < 0 || n_steps < 1 || (int64_t)start_pos[b] + n_steps > m->max_seq)
+      return fail(MKD_E_INVALID, "need start_pos >= 0, n_steps >= 1, start_pos + n_steps <= max_seq");
+  }
   if (!tokens_out_dev) return fail(MKD_E_INVALID, "null tokens_out_dev");
   if (m->trace && m->trace_cap < (size_t)m->n_wg * n_steps * m->max_instr * kTraceWords)
     return fail(MKD_E_INVALID, "trace buffer too small for this launch");
@@ -456,13 +516,21 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   p.trace = m->trace;
   p.watchdog_ticks = m->watchdog_ticks;
   p.n_wg = m->n_wg; p.max_instr = m->max_instr; p.n_chunks = m->n_chunks; p.n_lm_tiles = m->n_lm;
-  p.first_token = first_token; p.start_pos = start_pos; p.n_steps = n_steps; p.max_seq = m->max_seq;
+  p.n_steps = n_steps; p.max_seq = m->max_seq;
+  p.B = m->batch;
+  for (int b = 0; b < m->batch; ++b) {
+    p.first_tok[b] = first_tokens[b];
+    p.start[b] = start_pos[b];
+  }
+  p.s_qkv = m->s_qkv; p.s_part = m->s_part;
+  p.s_kv = (int64_t)c->n_layers * 2 * c->n_kv_heads * m->max_seq * c->head_dim;
   p.L = c->n_layers; p.d = c->d_model; p.hq = c->n_q_heads; p.hkv = c->n_kv_heads; p.hd = c->head_dim;
   p.F = c->d_ff; p.V = c->vocab; p.E = c->n_experts; p.topk = c->top_k;
   p.qd = c->n_q_heads * c->head_dim; p.kvd = c->n_kv_heads * c->head_dim;
   p.G = c->n_q_heads / c->n_kv_heads; p.tied = c->tied; p.lslots = layer_slots(c);
   p.x_floats = m->x_floats;
   p.out_floats = m->out_floats;
+  p.res_floats = m->res_floats;
   p.pre_units = m->pre_units;
   p.eps = c->rms_eps;
   const char* why = "";
@@ -472,6 +540,19 @@ int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_s
   if ((e = hipEventRecord(m->done, (hipStream_t)stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   m->launched = true;
   return MKD_OK;
+}
+
+int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_steps,
+               const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev, void* stream) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (m->batch != 1) return fail(MKD_E_INVALID, "the model decodes several sequences: use mkd_decode_batch");
+  return decode_launch(m, &first_token, &start_pos, n_steps, forced_dev, tokens_out_dev, logits_out_dev, stream);
+}
+
+int mkd_decode_batch(mkd_model* m, const int32_t* first_tokens, const int32_t* start_pos, int32_t n_steps,
+                     int32_t* tokens_out_dev, float* logits_out_dev, void* stream) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  return decode_launch(m, first_tokens, start_pos, n_steps, nullptr, tokens_out_dev, logits_out_dev, stream);
 }
 
 int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out) {

@@ -10,9 +10,10 @@
 
 namespace mkd {
 
-// ---------------------------------------------------------------- schedule spec v3
+// ---------------------------------------------------------------- schedule spec v4
 constexpr int32_t kMagic = 0x314B444D;
-constexpr int32_t kVersion = 3;
+constexpr int32_t kVersion = 4;
+constexpr int kMaxBatch = 8;  // sequences decoded together
 constexpr int kWords = 16;  // words per header and per instruction
 enum Opcode : int32_t {
   OP_NOP = 0,
@@ -28,10 +29,10 @@ enum Opcode : int32_t {
 };
 // instruction word indices
 enum : int { I_OP = 0, I_LAYER, I_STAGE, I_INDEX, I_A, I_B, I_WAIT_STAGE, I_WAIT_COUNT,
-             I_WAIT_PREV, I_SIGNAL };
+             I_WAIT_PREV, I_SIGNAL, I_SEQ };
 // header word indices
 enum : int { H_MAGIC = 0, H_VERSION, H_NWG, H_NSTAGES, H_MAXINSTR, H_NCHUNKS, H_L, H_D, H_HQ,
-             H_HKV, H_HD, H_F, H_V, H_E, H_TOPK, H_TOTAL };
+             H_HKV, H_HD, H_F, H_V, H_E, H_TOPK, H_BATCH };
 
 struct StageDesc {
   int32_t op, layer, size;  // size: rows (GEMV) or instruction count
@@ -39,12 +40,12 @@ struct StageDesc {
 
 // host-side schedule helpers (schedule.cpp)
 int config_check(const mkd_config* c, const char** why);
-void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, int cap);
+void stage_list(const mkd_config* c, int n_chunks, int batch, StageDesc* out, int* n_out, int cap);
 int stage_count(const mkd_config* c, int n_chunks);
 // blocks stage s may use, and the first of them (spec v3 placement)
 void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, int* first);
 bool is_tiled(int op);  // stages whose instructions are row tiles
-int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, size_t cap,
+int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int batch, int32_t* out, size_t cap,
                    size_t* n_words, const char** why);
 int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const char** why);
 
@@ -89,10 +90,21 @@ struct KParams {
   uint64_t* trace;           // or null
   uint64_t watchdog_ticks;
   int32_t n_wg, max_instr, n_chunks, n_lm_tiles, n_stages, flag_stride;
-  int32_t first_token, start_pos, n_steps, max_seq;
+  int32_t n_steps, max_seq;
+  // Batch: B sequences decoded together.  The inputs of row-tiled
+  // instructions (h, aout, hmid, act) and the LM-head partials (lm) hold
+  // element r of sequence b at word r * B + b; qkv and part, read per
+  // sequence by attention, hold sequence b at b * s_qkv (b * s_part); the
+  // cache holds sequence b at element b * s_kv.
+  int32_t B;
+  int32_t first_tok[kMaxBatch];       // token of step 0, per sequence
+  int32_t start[kMaxBatch];           // position of step 0, per sequence
+  int32_t s_qkv, s_part;              // words
+  int64_t s_kv;                       // bf16 elements
   int32_t L, d, hq, hkv, hd, F, V, E, topk, qd, kvd, G, tied, lslots;
   int32_t x_floats;          // LDS floats reserved for the staged input vector
   int32_t out_floats;        // LDS floats for one instruction's GEMV row results
+  int32_t res_floats;        // LDS floats for the residual rows of a tile (all sequences)
   int32_t pre_units;         // dense gate/up: 1 KiB weight units per wavefront staged in LDS
                              // by the instruction before it (0 = none)
   float eps;
@@ -102,6 +114,7 @@ size_t lds_bytes(const KParams& p);
 // launch the reset kernel and the cooperative megakernel on `stream`
 // ev0/ev1 (may be null) are recorded around the cooperative kernel alone
 int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why);
-int max_coop_blocks(int device, size_t lds, int* out);
+// co-resident workgroups of the persistent kernel for `batch` sequences
+int max_coop_blocks(int device, size_t lds, int batch, int* out);
 
 }  // namespace mkd

@@ -153,13 +153,16 @@ __device__ __forceinline__ const uint16_t* lptr(CKParams& p, int layer, int slot
 struct Ctx {
   CKParams& p;
   float* xs;     // staged input vector   [x_floats]
-  float* res;    // residual rows         [d]
+  float* res;    // residual rows         [res_floats]
   float* out;    // GEMV row results      [out_floats]
   float* red;    // reduction scratch     [kRed]
   lds_vint* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
   int wg, instr, t, tid, lane, wave;
   int stage, index, wait_stage, wait_count, wait_prev;  // from the instruction words
   uint64_t* tr;                                  // this instruction's trace entry, or null
+  int seq;                                       // sequence of a per-sequence instruction
+  int B;                                         // sequences decoded together (a constant 1
+                                                 // in the batch-1 kernel)
 };
 
 // Record a device error: the first raiser records where; with stop_all every
@@ -468,19 +471,17 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// argmax of step tt's logits from the LM-head tile partials
-__device__ __forceinline__ int fold_argmax(Ctx& c, int tt, bool* ok) {
+// argmax of sequence sq's logits from the LM-head tile partials staged in
+// LDS at xs: (max, argmax) pairs in tile order, the sequences interleaved
+// (word w of sequence sq at xs[w * B + sq])
+__device__ __forceinline__ int argmax_staged(Ctx& c, int sq) {
   CKParams& p = c.p;
-  const Fetch f[1] = {{p.lm, 2 * p.n_lm_tiles, tag_of(p, tt, p.L), c.xs}};
-  if (!gather<1>(c, f, p.n_stages - 1, (uint32_t)(tt + 1), p.n_lm_tiles)) {
-    *ok = false;
-    return 0;
-  }
+  const int B = c.B;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for (int k = c.tid; k < p.n_lm_tiles; k += kThreads) {
-    const float v = c.xs[2 * k];
-    const int i = __float_as_int(c.xs[2 * k + 1]);
+    const float v = c.xs[(2 * k) * B + sq];
+    const int i = __float_as_int(c.xs[(2 * k + 1) * B + sq]);
     if (better(v, i, bv, bi)) { bv = v; bi = i; }
   }
 #pragma unroll
@@ -497,38 +498,54 @@ __device__ __forceinline__ int fold_argmax(Ctx& c, int tt, bool* ok) {
   for (int w = 1; w < kWaves; ++w)
     if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
   __syncthreads();
-  *ok = true;
   return uni(bi);
 }
 
-// token consumed at step t (cached per step in LDS)
-__device__ __forceinline__ int step_token(Ctx& c, bool* ok) {
+// every sequence's LM-head tile partials of step tt, staged in LDS at xs;
+// waits for the LM-head stage first
+__device__ __forceinline__ bool fetch_partials(Ctx& c, int tt) {
   CKParams& p = c.p;
-  *ok = true;
-  if (uni(c.sflag[2]) == c.t) return uni(c.sflag[1]);
-  int tok;
+  const Fetch f[1] = {{p.lm, 2 * p.n_lm_tiles * c.B, tag_of(p, tt, p.L), c.xs}};
+  return gather<1>(c, f, p.n_stages - 1, (uint32_t)(tt + 1), p.n_lm_tiles);
+}
+
+__shared__ int s_tok[kMaxBatch];  // every sequence's token of step sflag[2]
+
+// tokens consumed at step t by every sequence, into s_tok (computed once per
+// step and workgroup; workgroup 0 records the previous step's argmax)
+__device__ __forceinline__ bool step_tokens(Ctx& c) {
+  CKParams& p = c.p;
+  if (uni(c.sflag[2]) == c.t) return true;
+  __syncthreads();  // every thread is done with the previous step's tokens
   if (c.t == 0) {
-    tok = p.first_token;
+    if (c.tid == 0)
+      for (int b = 0; b < c.B; ++b) s_tok[b] = p.first_tok[b];
   } else {
+    // teacher forcing (one sequence): workgroup 0 still folds the argmax to record it
     const int f = p.forced ? uni(ld_i32(p.forced + c.t)) : -1;
-    int am = 0;
     if (f < 0 || c.wg == 0) {
-      am = fold_argmax(c, c.t - 1, ok);
-      if (!*ok) return 0;
-      if (c.wg == 0 && c.tid == 0) st_i32(p.tokens_out + c.t - 1, am);
+      if (!fetch_partials(c, c.t - 1)) return false;
+      for (int b = 0; b < c.B; ++b) {
+        const int am = argmax_staged(c, b);
+        if (c.tid == 0) {
+          if (c.wg == 0) st_i32(p.tokens_out + (size_t)b * p.n_steps + c.t - 1, am);
+          if (f < 0) s_tok[b] = am;
+        }
+      }
     }
-    tok = f >= 0 ? f : am;
+    if (f >= 0 && c.tid == 0) s_tok[0] = f;
   }
-  if (tok < 0 || tok >= p.V) {
+  __syncthreads();
+  bool bad = false;
+  for (int b = 0; b < c.B; ++b) bad = bad || s_tok[b] < 0 || s_tok[b] >= p.V;
+  if (bad) {
     if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
     __syncthreads();
-    *ok = false;
-    return 0;
+    return false;
   }
+  if (c.tid == 0) c.sflag[2] = c.t;
   __syncthreads();
-  if (c.tid == 0) { c.sflag[1] = tok; c.sflag[2] = c.t; }
-  __syncthreads();
-  return tok;
+  return true;
 }
 
 // ---------------------------------------------------------------- GEMV row streamer
@@ -676,66 +693,68 @@ struct GenMap {
 
 constexpr int kNoSplit = 0x7fffffff;
 
-// the embedding row of this step's token, rows [r0, r1), into dst
+// the embedding rows [r0, r1) of every sequence's token of this step, into
+// dst interleaved (row r of sequence b at dst[(r - r0) * B + b])
 __device__ __forceinline__ bool embed_rows(Ctx& c, int r0, int r1, float* dst) {
   CKParams& p = c.p;
-  bool ok;
-  const int tok = step_token(c, &ok);
-  if (!ok) return false;
-  const uint16_t* e = wptr(p, W_EMBED) + (size_t)tok * p.d;
-  for (int i = r0 + c.tid; i < r1; i += kThreads) dst[i - r0] = bf_val(ld_u16(e + i));
+  if (!step_tokens(c)) return false;
+  const int B = c.B;
+  for (int b = 0; b < B; ++b) {
+    const uint16_t* e = wptr(p, W_EMBED) + (size_t)s_tok[b] * p.d;
+    for (int i = r0 + c.tid; i < r1; i += kThreads) dst[(i - r0) * B + b] = bf_val(ld_u16(e + i));
+  }
   return true;
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// LM-head epilogue: logits out, and this tile's (max, lowest argmax)
+// LM-head epilogue: logits out, and this tile's (max, lowest argmax), for
+// every sequence (row i of sequence sq is out[i * NB + sq])
+template <int NB>
 __device__ __forceinline__ void lmhead_epilogue(Ctx& c, int a, int b, int index) {
   CKParams& p = c.p;
-  float* logits = p.logits_out ? p.logits_out + (size_t)c.t * p.V + a : nullptr;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  int fin = 1;
-  for (int i = c.tid; i < b - a; i += kThreads) {
-    const float v = c.out[i];
-    if (logits) st_f32(logits + i, v);
-    fin &= isfinite(v) ? 1 : 0;
-    if (better(v, a + i, bv, bi)) { bv = v; bi = a + i; }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    fin &= __shfl_xor(fin, off);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  int* ired = (int*)(c.red + 64);
-  if (c.lane == 0) {
-    c.red[c.wave] = bv;
-    ired[c.wave] = bi;
-    ired[16 + c.wave] = fin;
-  }
-  __syncthreads();
-  if (c.tid == 0) {
-    bv = c.red[0];
-    bi = ired[0];
-    bool all_fin = ired[16] != 0;
-    for (int w = 1; w < kWaves; ++w) {
-      if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
-      all_fin = all_fin && ired[16 + w] != 0;
+  for (int sq = 0; sq < NB; ++sq) {
+    float* logits = p.logits_out ? p.logits_out + ((size_t)sq * p.n_steps + c.t) * p.V + a : nullptr;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    int fin = 1;
+    for (int i = c.tid; i < b - a; i += kThreads) {
+      const float v = c.out[i * NB + sq];
+      if (logits) st_f32(logits + i, v);
+      fin &= isfinite(v) ? 1 : 0;
+      if (better(v, a + i, bv, bi)) { bv = v; bi = a + i; }
     }
-    if (!all_fin) raise_error(c, MKD_E_NONFINITE, false);
-    const uint32_t tag = tag_of(p, c.t, p.L);
-    ll_store(p.lm + 2 * index, bv, tag);
-    ll_store(p.lm + 2 * index + 1, __int_as_float(bi), tag);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      fin &= __shfl_xor(fin, off);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    int* ired = (int*)(c.red + 64);
+    if (c.lane == 0) {
+      c.red[c.wave] = bv;
+      ired[c.wave] = bi;
+      ired[16 + c.wave] = fin;
+    }
+    __syncthreads();
+    if (c.tid == 0) {
+      bv = c.red[0];
+      bi = ired[0];
+      bool all_fin = ired[16] != 0;
+      for (int w = 1; w < kWaves; ++w) {
+        if (better(c.red[w], ired[w], bv, bi)) { bv = c.red[w]; bi = ired[w]; }
+        all_fin = all_fin && ired[16 + w] != 0;
+      }
+      if (!all_fin) raise_error(c, MKD_E_NONFINITE, false);
+      const uint32_t tag = tag_of(p, c.t, p.L);
+      ll_store(p.lm + (size_t)(2 * index) * NB + sq, bv, tag);
+      ll_store(p.lm + (size_t)(2 * index + 1) * NB + sq, __int_as_float(bi), tag);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
-// RMSNorm + QKV, O-proj + residual, RMSNorm + gate/up + SiLU, down + residual
-// and RMSNorm + LM head: one code path, the opcode only picks matrices,
-// inputs and the epilogue.  Weights for the first RING loads per lane are
-// requested before the inputs are waited for.
 __device__ __forceinline__ void desc_init(GemvDesc& g, int a, int w) {
   g.b00 = g.b01 = g.b02 = g.b10 = g.b11 = g.b12 = nullptr;
   g.s1 = g.s2 = kNoSplit;
@@ -790,9 +809,9 @@ __device__ __forceinline__ void stage_upgate(Ctx& c, int l, int a, int b) {
 
 // Matrices, inputs and norm gains of one dense GEMV instruction (the opcode
 // picks them; everything else is shared): the row map g, the tagged inputs
-// f (vector, residual rows), the RMSNorm gains of the vector (or null) and
-// whether the vector (layer 0 QKV) or the residual rows (layer 0 O-proj)
-// come from the embedding instead.
+// f (vector, residual rows; every sequence's, interleaved), the RMSNorm
+// gains of the vector (or null) and whether the vector (layer 0 QKV) or the
+// residual rows (layer 0 O-proj) come from the embedding instead.
 __device__ __forceinline__ void gemv_setup(Ctx& c, int op, int l, int a, int b, uint32_t tag, GemvDesc& g,
                                            Fetch (&f)[2], const uint16_t*& gamma, bool& embed_x,
                                            bool& embed_res) {
@@ -802,39 +821,42 @@ __device__ __forceinline__ void gemv_setup(Ctx& c, int op, int l, int a, int b, 
   f[0] = {p.h, 0, tag, c.xs};
   f[1] = {p.h, 0, tag, c.res};
   embed_x = embed_res = false;
+  const int B = c.B;
   switch (op) {
     case OP_QKV:
       g.b00 = lptr(p, l, WL_Q); g.b01 = lptr(p, l, WL_K); g.b02 = lptr(p, l, WL_V);
       g.s1 = p.qd; g.s2 = p.qd + p.kvd; g.K = p.d;
       gamma = lptr(p, l, WL_ATTN_NORM);
       if (l == 0) embed_x = true;
-      else f[0] = {p.h, p.d, tag, c.xs};
+      else f[0] = {p.h, p.d * B, tag, c.xs};
       break;
     case OP_OPROJ:
       g.b00 = lptr(p, l, WL_O); g.K = p.qd;
-      f[0] = {p.aout, p.qd, tag, c.xs};
+      f[0] = {p.aout, p.qd * B, tag, c.xs};
       if (l == 0) embed_res = true;
-      else f[1] = {p.h + a, b - a, tag, c.res};   // published by the previous layer
+      else f[1] = {p.h + (size_t)a * B, (b - a) * B, tag, c.res};   // published by the previous layer
       break;
     case OP_UPGATE:
       desc_upgate(p, l, g);
       gamma = lptr(p, l, WL_FFN_NORM);
-      f[0] = {p.hmid, p.d, tag, c.xs};
+      f[0] = {p.hmid, p.d * B, tag, c.xs};
       break;
     case OP_DOWN:
       g.b00 = lptr(p, l, WL_DOWN); g.K = p.F;
-      f[0] = {p.act, p.F, tag, c.xs};
-      f[1] = {p.hmid + a, b - a, tag, c.res};
+      f[0] = {p.act, p.F * B, tag, c.xs};
+      f[1] = {p.hmid + (size_t)a * B, (b - a) * B, tag, c.res};
       break;
     default:  // OP_LMHEAD
       g.b00 = wptr(p, p.tied ? W_EMBED : W_LM_HEAD); g.K = p.d;
       gamma = wptr(p, W_FINAL_NORM);
-      f[0] = {p.h, p.d, tag, c.xs};
+      f[0] = {p.h, p.d * B, tag, c.xs};
       break;
   }
 }
 
-// stage the instruction's input vector in LDS (xs, and the residual rows in res)
+// stage the instruction's input vectors in LDS (xs, and the residual rows in
+// res), every sequence's interleaved; xs is zero from K up to the next
+// multiple of 512 (the streamers read whole 512-element segments)
 __device__ __forceinline__ bool gemv_inputs(Ctx& c, int a, int b, int K, const Fetch (&f)[2], bool embed_x,
                                             bool embed_res) {
   CKParams& p = c.p;
@@ -849,33 +871,44 @@ __device__ __forceinline__ bool gemv_inputs(Ctx& c, int a, int b, int K, const F
     if (!gather_inputs<2>(c, f)) return false;
   }
   if (K & 511) {
-    pad_zero(c, c.xs, K);
+    const int B = c.B;
+    for (int i = K * B + c.tid; i < ((K + 511) & ~511) * B; i += kThreads) c.xs[i] = 0.f;
     __syncthreads();
   }
   return true;
 }
 
-// write the instruction's outputs from the row results in LDS
+// write the instruction's outputs from the row results in LDS (row i of
+// sequence sq at out[i * NB + sq]; the gate/up opcode's row i has its gate
+// result at row 2i and its up result at row 2i + 1)
+template <int NB>
 __device__ __forceinline__ void gemv_epilogue(Ctx& c, int op, int l, int a, int b, int index, uint32_t tag) {
   CKParams& p = c.p;
+  const int n = (b - a) * NB;
+  const size_t o = (size_t)a * NB;
   switch (op) {
     case OP_QKV:
-      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.qkv + a + i, c.out[i], tag);
+      for (int j = c.tid; j < n; j += kThreads) {
+        const int i = j / NB, sq = j - i * NB;
+        ll_store(p.qkv + (size_t)sq * p.s_qkv + a + i, c.out[j], tag);
+      }
       break;
     case OP_OPROJ:
-      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.hmid + a + i, c.res[i] + c.out[i], tag);
+      for (int j = c.tid; j < n; j += kThreads) ll_store(p.hmid + o + j, c.res[j] + c.out[j], tag);
       break;
     case OP_UPGATE:
-      for (int i = c.tid; i < b - a; i += kThreads)
-        ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
+      for (int j = c.tid; j < n; j += kThreads) {
+        const int i = j / NB, sq = j - i * NB;
+        ll_store(p.act + o + j, silu(c.out[2 * i * NB + sq]) * c.out[(2 * i + 1) * NB + sq], tag);
+      }
       break;
     case OP_DOWN: {
       const uint32_t otag = tag_of(p, c.t, l + 1);
-      for (int i = c.tid; i < b - a; i += kThreads) ll_store(p.h + a + i, c.res[i] + c.out[i], otag);
+      for (int j = c.tid; j < n; j += kThreads) ll_store(p.h + o + j, c.res[j] + c.out[j], otag);
       break;
     }
     default:
-      lmhead_epilogue(c, a, b, index);
+      lmhead_epilogue<NB>(c, a, b, index);
       break;
   }
 }
@@ -908,7 +941,7 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
   rs.run(c.xs, c.out, pre_area(c));
   mark_computed(c);
   __syncthreads();
-  gemv_epilogue(c, op, l, a, b, index, tag);
+  gemv_epilogue<1>(c, op, l, a, b, index, tag);
   return true;
 }
 
@@ -1089,13 +1122,187 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   }
   mark_computed(c);
   __syncthreads();
-  gemv_epilogue(c, op, l, a, b, index, tag);
+  gemv_epilogue<1>(c, op, l, a, b, index, tag);
   return true;
 }
 
-// dense GEMV opcodes: the compile-time row length when there is one
+// ---------------------------------------------------------------- several sequences
+
+// xs[i * NB + b] <- rmsnorm of sequence b's vector (element i), times gamma[i]
+template <int NB>
+__device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma) {
+  float ss[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+  for (int i = c.tid; i < d; i += kThreads)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) ss[b] = fmaf(c.xs[i * NB + b], c.xs[i * NB + b], ss[b]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float w = wave_sum(ss[b]);
+    if (c.lane == 0) c.red[b * kWaves + c.wave] = w;
+  }
+  __syncthreads();
+  float inv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += c.red[b * kWaves + w];
+    inv[b] = 1.0f / sqrtf(tot / (float)d + c.p.eps);
+  }
+  for (int i = c.tid; i < d; i += kThreads) {
+    const float g = bf_val(ld_u16(gamma + i));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) c.xs[i * NB + b] = (c.xs[i * NB + b] * inv[b]) * g;
+  }
+  __syncthreads();
+}
+
+// Rows of one instruction dotted with NB input vectors at once.  The inputs
+// sit interleaved in LDS (element k of sequence b at xs[k * NB + b]), so
+// the slice a lane needs for one 16-byte weight load (8 elements) is 8 NB
+// contiguous floats.  A wavefront takes its stream rows in groups of G and
+// walks a group segment by segment: each ring step holds the G rows' units
+// of one segment, and one read of the input slice serves all G of them
+// (LDS traffic per weight byte falls by G).  The ring is D steps deep (G D
+// units, 8 KiB per wavefront in flight).  Loads past the last row use
+// zero-size descriptors, so every refill is issued without a branch.
+template <int NB>
+struct BatchStream {
+  static constexpr int G = 4, D = 2;
+  const GenMap& m;
+  const int K, nseg, ns, steps;
+  const uint32_t lane16;
+  int pseg, pg;                     // producer: segment, group
+  __amdgpu_buffer_rsrc_t pr[G];     // the producer group's row descriptors
+  u32x4 ring[D][G];
+
+  __device__ __forceinline__ BatchStream(const GenMap& m_, int K_, int ns_, int lane)
+      : m(m_), K(uni(K_)), nseg(uni((K_ + 511) >> 9)), ns(uni(ns_)),
+        steps(uni(((ns_ + G - 1) / G) * ((K_ + 511) >> 9))), lane16((uint32_t)lane * 16u), pseg(0), pg(0) {
+    set_group();
+  }
+  __device__ __forceinline__ void set_group() {
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const int k = pg * G + r;
+      const bool live = k < ns;
+      pr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(m.row(live ? k : 0)), (short)0,
+                                                live ? 2 * K : 0, (int)kBufFlags);
+    }
+  }
+  __device__ __forceinline__ void issue(u32x4 (&dst)[G]) {
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(pr[r], (int)lane16, pseg * 1024, kNT);
+    if (++pseg == nseg) {
+      pseg = 0;
+      ++pg;
+      set_group();
+    }
+  }
+  __device__ __forceinline__ void prefetch() {
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ring[d]);
+  }
+  __device__ __forceinline__ void run(const float* xs, float* out) {
+    const float* xl = xs + lane16 / 16u * 8 * NB;
+    float acc[G][NB];
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+    int cseg = 0, cg = 0;
+    auto eat = [&](const u32x4 (&w)[G]) {
+      const f32x4* xp = (const f32x4*)(xl + cseg * 512 * NB);
+      float x[8 * NB];
+#pragma unroll
+      for (int q = 0; q < 2 * NB; ++q) {
+        const f32x4 v = xp[q];
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const uint32_t wr[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float wj = (j & 1) ? bf_hi(wr[j >> 1]) : bf_lo(wr[j >> 1]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[r][b] = fmaf(wj, x[j * NB + b], acc[r][b]);
+        }
+      }
+      if (++cseg == nseg) {
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+          const int k = cg * G + r;
+          const int o = m.slot(k) * NB;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float v = wave_sum(acc[r][b]);
+            if (k < ns) out[o + b] = v;
+            acc[r][b] = 0.f;
+          }
+        }
+        cseg = 0;
+        ++cg;
+      }
+    };
+    for (int s0 = 0; s0 < steps; s0 += D) {
+      if (s0 + D < steps) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          eat(ring[d]);
+          issue(ring[d]);
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+          if (s0 + d < steps) eat(ring[d]);
+      }
+    }
+  }
+};
+
+// One dense GEMV instruction for NB sequences: the same rows, inputs and
+// epilogues as with one sequence, every activation interleaved by sequence.
+template <int NB>
+__device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, int index) {
+  CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
+  GemvDesc g;
+  Fetch f[2];
+  const uint16_t* gamma;
+  bool embed_x, embed_res;
+  gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
+  const GenMap m{g};
+  BatchStream<NB> bs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane);
+  bs.prefetch();
+  if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
+  if (gamma) rmsnorm_b<NB>(c, p.d, gamma);
+  bs.run(c.xs, c.out);
+  mark_computed(c);
+  __syncthreads();
+  gemv_epilogue<NB>(c, op, l, a, b, index, tag);
+  return true;
+}
+
+// dense GEMV opcodes: several sequences (batched kernel) by their count;
+// one sequence by the compile-time row length when there is one
+template <bool BATCHED>
 __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b, int index) {
   CKParams& p = c.p;
+  if constexpr (BATCHED) {
+    switch (c.B) {
+      case 2: return op_gemv_b<2>(c, op, l, a, b, index);
+      case 3: return op_gemv_b<3>(c, op, l, a, b, index);
+      case 4: return op_gemv_b<4>(c, op, l, a, b, index);
+      case 5: return op_gemv_b<5>(c, op, l, a, b, index);
+      case 6: return op_gemv_b<6>(c, op, l, a, b, index);
+      case 7: return op_gemv_b<7>(c, op, l, a, b, index);
+      default: return op_gemv_b<8>(c, op, l, a, b, index);
+    }
+  }
   const int K = op == OP_OPROJ ? p.qd : (op == OP_DOWN ? p.F : p.d);
   switch ((K + 511) >> 9) {
     case 1: return op_gemv_fast<1>(c, op, l, a, b, index);
@@ -1234,7 +1441,8 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   CKParams& p = c.p;
   constexpr int LPR = HD / 8;     // lanes per K/V row
   constexpr int PPW = 64 / LPR;   // positions per wavefront load
-  const int pos = p.start_pos + c.t;
+  const int seq = c.seq;
+  const int pos = p.start[seq] + c.t;
   const int T = pos + 1;
   const int clen = ((T + p.n_chunks - 1) / p.n_chunks + 15) / 16 * 16;
   const int lo = min(T, chunk * clen), hi = min(T, (chunk + 1) * clen);
@@ -1244,8 +1452,9 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   const int grp = c.lane / LPR, sub = c.lane % LPR;
 
   const size_t head_elems = (size_t)p.max_seq * HD;
-  const uint16_t* kb = p.kv + ((size_t)(l * 2 + 0) * p.hkv + kvh) * head_elems;
-  const uint16_t* vb = p.kv + ((size_t)(l * 2 + 1) * p.hkv + kvh) * head_elems;
+  uint16_t* const kvs = p.kv + (size_t)seq * p.s_kv;   // this sequence's cache
+  const uint16_t* kb = kvs + ((size_t)(l * 2 + 0) * p.hkv + kvh) * head_elems;
+  const uint16_t* vb = kvs + ((size_t)(l * 2 + 1) * p.hkv + kvh) * head_elems;
   const uint32_t hbytes = (uint32_t)(head_elems * 2);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, hbytes), vr = make_rsrc(vb, hbytes);
 
@@ -1279,9 +1488,10 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   const int re = c.tid < (G + 1) * (HD / 2) ? c.tid : 0;
   const float cs = ld_f32(p.rope + (size_t)pos * (HD / 2) + re % (HD / 2));
   const float sn = ld_f32(p.rope + (size_t)p.max_seq * (HD / 2) + (size_t)pos * (HD / 2) + re % (HD / 2));
-  const Fetch f[3] = {{p.qkv + q0 * HD, G * HD, tag, qs},
-                      {p.qkv + p.qd + kvh * HD, HD, tag, ks},
-                      {p.qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
+  const uint64_t* qkv = p.qkv + (size_t)seq * p.s_qkv;
+  const Fetch f[3] = {{qkv + q0 * HD, G * HD, tag, qs},
+                      {qkv + p.qd + kvh * HD, HD, tag, ks},
+                      {qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
   if (!gather_inputs<3>(c, f)) return false;
 
   // RoPE (pairs i, i + HD/2) on q heads and k; q pre-scaled for exp2 softmax
@@ -1435,9 +1645,9 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
     }
     const int qh = q0 + g;
     if (p.n_chunks == 1) {
-      ll_store(p.aout + qh * HD + i, O / L, otag);
+      ll_store(p.aout + (size_t)(qh * HD + i) * c.B + seq, O / L, otag);
     } else {
-      uint64_t* pp = p.part + ((size_t)qh * p.n_chunks + chunk) * (HD + 2);
+      uint64_t* pp = p.part + (size_t)seq * p.s_part + ((size_t)qh * p.n_chunks + chunk) * (HD + 2);
       ll_store(pp + 2 + i, O, otag);
       if (i == 0) {
         ll_store(pp + 0, M, otag);
@@ -1469,7 +1679,7 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
   CKParams& p = c.p;
   const int HD = p.hd, n = p.n_chunks, W = HD + 2;
   const uint32_t tag = tag_of(p, c.t, l);
-  const Fetch f[1] = {{p.part + (size_t)qh * n * W, n * W, tag, c.xs}};
+  const Fetch f[1] = {{p.part + (size_t)c.seq * p.s_part + (size_t)qh * n * W, n * W, tag, c.xs}};
   if (!gather_inputs<1>(c, f)) return false;
   for (int i = c.tid; i < HD; i += kThreads) {
     float M = -INFINITY;
@@ -1480,7 +1690,7 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
       L = fmaf(c.xs[k * W + 1], a, L);
       O = fmaf(c.xs[k * W + 2 + i], a, O);
     }
-    ll_store(p.aout + qh * HD + i, O / L, tag);
+    ll_store(p.aout + (size_t)(qh * HD + i) * c.B + c.seq, O / L, tag);
   }
   __syncthreads();
   return true;
@@ -1490,11 +1700,15 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
 
 __shared__ int s_flags[8];
 
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams params) {
+// The persistent loop.  Two kernels instantiate it: one sequence (batch
+// size the constant 1, every opcode) and several (batch size from the
+// parameters, dense opcodes only), so that neither carries the other's
+// register pressure.
+template <bool BATCHED>
+__device__ __forceinline__ void megakernel_body() {
   // The parameters are read in place in the kernel-argument segment (they
   // are the first and only argument): referring to the by-value parameter
   // itself would make the compiler copy it to scratch memory.
-  (void)params;
   CKParams* pk = (CKParams*)__builtin_amdgcn_kernarg_segment_ptr();
   extern __shared__ __align__(16) float smem[];
   lds_vint* sflag = (lds_vint*)s_flags;
@@ -1522,10 +1736,11 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
                 b = ldc_i32(ins + I_B), index = ldc_i32(ins + I_INDEX);
       uint64_t* tr = p.trace ? p.trace + (((size_t)wg * p.n_steps + t) * p.max_instr + i) * kTraceWords
                              : nullptr;
-      Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
+      Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.res_floats,
+            smem + p.x_floats + p.res_floats + p.out_floats,
             sflag, wg, i, t, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6),
             ldc_i32(ins + I_STAGE), index, ldc_i32(ins + I_WAIT_STAGE), ldc_i32(ins + I_WAIT_COUNT),
-            ldc_i32(ins + I_WAIT_PREV), tr};
+            ldc_i32(ins + I_WAIT_PREV), tr, BATCHED ? ldc_i32(ins + I_SEQ) : 0, BATCHED ? p.B : 1};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
       // Dense gate/up weights are staged in LDS by the instruction before
       // them: at the start of an O-projection (whose wait spans the whole
@@ -1539,11 +1754,15 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
         case OP_OPROJ:
         case OP_UPGATE:
         case OP_DOWN:
-        case OP_LMHEAD: ok = op_gemv_any(c, op, l, a, b, index); break;
+        case OP_LMHEAD: ok = op_gemv_any<BATCHED>(c, op, l, a, b, index); break;
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
-        case OP_MOE_UPGATE: ok = op_moe_upgate(c, l, a, b, index); break;
-        case OP_MOE_DOWN: ok = op_moe_down(c, l, a, b); break;
+        case OP_MOE_UPGATE:
+          if constexpr (!BATCHED) ok = op_moe_upgate(c, l, a, b, index);
+          break;
+        case OP_MOE_DOWN:
+          if constexpr (!BATCHED) ok = op_moe_down(c, l, a, b);
+          break;
         default: break;
       }
       if (ok) signal_done(c);
@@ -1554,13 +1773,27 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams
   if (ok && wg == 0) {
     CKParams& p = *pk;
     const int tid = threadIdx.x;
-    Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.d, smem + p.x_floats + p.d + p.out_floats,
+    Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.res_floats,
+          smem + p.x_floats + p.res_floats + p.out_floats,
           sflag, wg, 0, p.n_steps, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6), 0, 0, 0, 0,
-          0, nullptr};
-    bool fok;
-    const int am = fold_argmax(c, p.n_steps - 1, &fok);
-    if (fok && tid == 0) st_i32(p.tokens_out + p.n_steps - 1, am);
+          0, nullptr, 0, BATCHED ? p.B : 1};
+    if (fetch_partials(c, p.n_steps - 1)) {
+      for (int b = 0; b < c.B; ++b) {
+        const int am = argmax_staged(c, b);
+        if (tid == 0) st_i32(p.tokens_out + (size_t)b * p.n_steps + p.n_steps - 1, am);
+      }
+    }
   }
+}
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams params) {
+  (void)params;
+  megakernel_body<false>();
+}
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel_batch(KParams params) {
+  (void)params;
+  megakernel_body<true>();
 }
 
 extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
@@ -1575,19 +1808,22 @@ extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
 // ---------------------------------------------------------------- host-side launch
 
 size_t lds_bytes(const KParams& p) {
-  return ((size_t)p.x_floats + (size_t)p.d + (size_t)p.out_floats + kRed) * sizeof(float) +
+  return ((size_t)p.x_floats + (size_t)p.res_floats + (size_t)p.out_floats + kRed) * sizeof(float) +
          (size_t)p.pre_units * kWaves * 1024;
 }
 
-int max_coop_blocks(int device, size_t lds, int* out) {
+// the persistent kernel for `batch` sequences
+static const void* kernel_for(int batch) {
+  return batch > 1 ? (const void*)mkd_megakernel_batch : (const void*)mkd_megakernel;
+}
+
+int max_coop_blocks(int device, size_t lds, int batch, int* out) {
   if (hipSetDevice(device) != hipSuccess) return MKD_E_HIP;
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)mkd_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
+  const void* k = kernel_for(batch);
+  if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return MKD_E_HIP;
   int per_cu = 0, n_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)mkd_megakernel, kThreads,
-                                                   lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, lds) != hipSuccess)
     return MKD_E_HIP;
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
     return MKD_E_HIP;
@@ -1603,9 +1839,8 @@ int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(mkd_reset, dim3(blocks), dim3(256), 0, s, p.h, ll_words, p.status);
   if (hipGetLastError() != hipSuccess) { *why = "reset kernel launch failed"; return MKD_E_HIP; }
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)mkd_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess) {
+  const void* k = kernel_for(p.B);
+  if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     *why = "cannot raise the kernel's LDS limit";
     return MKD_E_HIP;
   }
@@ -1621,10 +1856,8 @@ int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1
     return v && strcmp(v, "plain") == 0;
   }();
   const hipError_t e =
-      plain ? hipLaunchKernel((const void*)mkd_megakernel, dim3(p.n_wg), dim3(kThreads), args,
-                              (unsigned)lds, s)
-            : hipLaunchCooperativeKernel((const void*)mkd_megakernel, dim3(p.n_wg), dim3(kThreads),
-                                         args, (unsigned)lds, s);
+      plain ? hipLaunchKernel(k, dim3(p.n_wg), dim3(kThreads), args, (unsigned)lds, s)
+            : hipLaunchCooperativeKernel(k, dim3(p.n_wg), dim3(kThreads), args, (unsigned)lds, s);
   if (e == hipErrorCooperativeLaunchTooLarge) {
     *why = "grid does not fit co-resident on the device";
     return MKD_E_COOPERATIVE;

@@ -1,15 +1,19 @@
-// Host-side schedule builder and validator (schedule spec v3).
+// Host-side schedule builder and validator (schedule spec v4).
 //
 // The persistent kernel walks a host-built list of every operation of the
 // forward pass (Hyperkernel teardown, "What a megakernel buys"; Kittens VM
 // summary, "Method").  The pages fix no format, tiling or assignment; this
-// file implements this library's spec v3:
+// file implements this library's spec v4:
+//   a launch decodes B sequences together (batch B >= 1);
 //   stages per token: per layer QKV, ATTN, [AREDUCE if n_chunks > 1], OPROJ,
 //   UPGATE|MOE_UPGATE, DOWN|MOE_DOWN; then LMHEAD.
 //   Row-tiled stage over R rows: n = min(n_wg, R) tiles, tile i = [i*R/n, (i+1)*R/n).
 //   ATTN: one chunk -> hq instructions (one q head each); n_chunks > 1 ->
 //   hkv * n_chunks (kv_head = i / n_chunks, chunk = i % n_chunks), merged by
-//   AREDUCE (hq instructions).  Instruction i of a stage runs on block
+//   AREDUCE (hq instructions).  ATTN and AREDUCE repeat that for every
+//   sequence: instruction i serves sequence i / n (n per sequence, word
+//   I_SEQ) with the operands of instruction i % n.  Row-tiled instructions
+//   compute their rows for all B sequences.  Instruction i of a stage runs on block
 //   (offset + i) % n_wg; the offset is 0 except for OPROJ, whose tiles skip
 //   the blocks that ran the stage before it (ATTN, or AREDUCE) when there
 //   are more blocks than that stage has instructions: those blocks finish
@@ -56,7 +60,7 @@ int stage_count(const mkd_config* c, int n_chunks) {
   return c->n_layers * (n_chunks > 1 ? 6 : 5) + 1;
 }
 
-void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, int cap) {
+void stage_list(const mkd_config* c, int n_chunks, int batch, StageDesc* out, int* n_out, int cap) {
   int n = 0;
   auto push = [&](int op, int l, int sz) {
     if (n < cap) out[n] = StageDesc{op, l, sz};
@@ -65,8 +69,8 @@ void stage_list(const mkd_config* c, int n_chunks, StageDesc* out, int* n_out, i
   const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
   for (int l = 0; l < c->n_layers; ++l) {
     push(OP_QKV, l, qd + 2 * kvd);
-    push(OP_ATTN, l, n_chunks == 1 ? c->n_q_heads : c->n_kv_heads * n_chunks);
-    if (n_chunks > 1) push(OP_AREDUCE, l, c->n_q_heads);
+    push(OP_ATTN, l, batch * (n_chunks == 1 ? c->n_q_heads : c->n_kv_heads * n_chunks));
+    if (n_chunks > 1) push(OP_AREDUCE, l, batch * c->n_q_heads);
     push(OP_OPROJ, l, c->d_model);
     if (c->n_experts) {
       push(OP_MOE_UPGATE, l, c->top_k * c->d_ff);
@@ -98,42 +102,47 @@ void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, in
   }
 }
 
-static void operands(const StageDesc& s, int n_wg, int n_chunks, int i, int32_t* a, int32_t* b) {
+static void operands(const StageDesc& s, int n_wg, int n_chunks, int batch, int i, int32_t* a, int32_t* b,
+                     int32_t* seq) {
+  *seq = 0;
   if (is_tiled(s.op)) {
     const int64_t n = stage_ninstr(s, n_wg), R = s.size;
     *a = (int32_t)(i * R / n);
     *b = (int32_t)((i + 1) * R / n);
-  } else if (s.op == OP_ATTN) {
-    *a = n_chunks == 1 ? i : i / n_chunks;   // q head, or kv head
-    *b = n_chunks == 1 ? 0 : i % n_chunks;   // chunk
+    return;
+  }
+  const int per = s.size / batch;
+  *seq = i / per;
+  const int j = i % per;
+  if (s.op == OP_ATTN) {
+    *a = n_chunks == 1 ? j : j / n_chunks;   // q head, or kv head
+    *b = n_chunks == 1 ? 0 : j % n_chunks;   // chunk
   } else {  // AREDUCE
-    *a = i;
+    *a = j;
     *b = 0;
   }
 }
 
-int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, size_t cap,
+int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int batch, int32_t* out, size_t cap,
                    size_t* n_words, const char** why) {
   int rc = config_check(c, why);
   if (rc) return rc;
   if (n_wg < 1 || n_wg > 65536) { *why = "n_wg must be in [1, 65536]"; return MKD_E_INVALID; }
   if (n_chunks < 1 || n_chunks > 4096) { *why = "n_chunks must be in [1, 4096]"; return MKD_E_INVALID; }
+  if (batch < 1 || batch > kMaxBatch) { *why = "batch must be in [1, 8]"; return MKD_E_INVALID; }
   if (!n_words) { *why = "null n_words"; return MKD_E_INVALID; }
   const int n_st = stage_count(c, n_chunks);
   std::vector<StageDesc> st(n_st);
   int got = 0;
-  stage_list(c, n_chunks, st.data(), &got, n_st);
+  stage_list(c, n_chunks, batch, st.data(), &got, n_st);
   std::vector<int> cnt(n_st), avail(n_st), first(n_st);
   for (int s = 0; s < n_st; ++s) {
     placement(st, s, n_wg, &avail[s], &first[s]);
     cnt[s] = stage_ninstr(st[s], avail[s]);
   }
   std::vector<int> per_wg(n_wg, 0);
-  int64_t total = 0;
-  for (int s = 0; s < n_st; ++s) {
+  for (int s = 0; s < n_st; ++s)
     for (int i = 0; i < cnt[s]; ++i) ++per_wg[(first[s] + i) % n_wg];
-    total += cnt[s];
-  }
   int max_instr = 0;
   for (int w = 0; w < n_wg; ++w) max_instr = per_wg[w] > max_instr ? per_wg[w] : max_instr;
   const size_t words = (size_t)kWords + n_wg + (size_t)n_wg * max_instr * kWords;
@@ -146,7 +155,7 @@ int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, si
   hdr[H_MAXINSTR] = max_instr; hdr[H_NCHUNKS] = n_chunks; hdr[H_L] = c->n_layers;
   hdr[H_D] = c->d_model; hdr[H_HQ] = c->n_q_heads; hdr[H_HKV] = c->n_kv_heads;
   hdr[H_HD] = c->head_dim; hdr[H_F] = c->d_ff; hdr[H_V] = c->vocab; hdr[H_E] = c->n_experts;
-  hdr[H_TOPK] = c->top_k; hdr[H_TOTAL] = (int32_t)total;
+  hdr[H_TOPK] = c->top_k; hdr[H_BATCH] = batch;
   int32_t* counts = out + kWords;
   int32_t* body = counts + n_wg;
   std::vector<int> fill(n_wg, 0);
@@ -159,7 +168,7 @@ int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int32_t* out, si
       ins[I_LAYER] = st[s].layer;
       ins[I_STAGE] = s;
       ins[I_INDEX] = i;
-      operands(st[s], avail[s], n_chunks, i, &ins[I_A], &ins[I_B]);
+      operands(st[s], avail[s], n_chunks, batch, i, &ins[I_A], &ins[I_B], &ins[I_SEQ]);
       ins[I_WAIT_STAGE] = ws;
       ins[I_WAIT_COUNT] = cnt[ws];
       ins[I_WAIT_PREV] = s == 0 ? 1 : 0;
@@ -176,7 +185,10 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
   if (!w || n < (size_t)kWords) { *why = "schedule too short"; return MKD_E_INVALID; }
   if (w[H_MAGIC] != kMagic || w[H_VERSION] != kVersion) { *why = "bad magic/version"; return MKD_E_INVALID; }
   const int n_wg = w[H_NWG], n_st = w[H_NSTAGES], max_instr = w[H_MAXINSTR], n_chunks = w[H_NCHUNKS];
-  if (n_wg < 1 || max_instr < 0 || n_chunks < 1) { *why = "bad header"; return MKD_E_INVALID; }
+  const int batch = w[H_BATCH];
+  if (n_wg < 1 || max_instr < 0 || n_chunks < 1 || batch < 1 || batch > kMaxBatch) {
+    *why = "bad header"; return MKD_E_INVALID;
+  }
   if (n != (size_t)kWords + n_wg + (size_t)n_wg * max_instr * kWords) { *why = "size mismatch"; return MKD_E_INVALID; }
   if (w[H_L] != c->n_layers || w[H_D] != c->d_model || w[H_HQ] != c->n_q_heads ||
       w[H_HKV] != c->n_kv_heads || w[H_HD] != c->head_dim || w[H_F] != c->d_ff ||
@@ -186,7 +198,7 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
   if (n_st != stage_count(c, n_chunks)) { *why = "stage count"; return MKD_E_INVALID; }
   std::vector<StageDesc> st(n_st);
   int got = 0;
-  stage_list(c, n_chunks, st.data(), &got, n_st);
+  stage_list(c, n_chunks, batch, st.data(), &got, n_st);
   std::vector<int> cnt(n_st), avail(n_st), first(n_st);
   for (int s = 0; s < n_st; ++s) {
     placement(st, s, n_wg, &avail[s], &first[s]);
@@ -211,15 +223,17 @@ int schedule_validate(const mkd_config* c, const int32_t* w, size_t n, const cha
       if (i < 0 || i >= cnt[s] || (first[s] + i) % n_wg != b) { *why = "instruction index or block"; return MKD_E_INVALID; }
       if (seen[s][i]) { *why = "instruction repeated"; return MKD_E_INVALID; }
       seen[s][i] = 1;
-      int32_t a, bb;
-      operands(st[s], avail[s], n_chunks, i, &a, &bb);
-      if (ins[I_A] != a || ins[I_B] != bb) { *why = "operands differ from the spec"; return MKD_E_INVALID; }
+      int32_t a, bb, sq;
+      operands(st[s], avail[s], n_chunks, batch, i, &a, &bb, &sq);
+      if (ins[I_A] != a || ins[I_B] != bb || ins[I_SEQ] != sq) {
+        *why = "operands differ from the spec"; return MKD_E_INVALID;
+      }
       const int ws = s == 0 ? n_st - 1 : s - 1;
       if (ins[I_WAIT_STAGE] != ws || ins[I_WAIT_COUNT] != cnt[ws] || ins[I_WAIT_PREV] != (s == 0) ||
           ins[I_SIGNAL] != s) {
         *why = "wait/signal fields"; return MKD_E_INVALID;
       }
-      for (int k = I_SIGNAL + 1; k < kWords; ++k)
+      for (int k = I_SEQ + 1; k < kWords; ++k)
         if (ins[k] != 0) { *why = "reserved word not zero"; return MKD_E_INVALID; }
     }
   }

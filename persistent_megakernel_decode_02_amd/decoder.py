@@ -11,15 +11,18 @@ from . import capi
 
 class Decoder:
     """One model on one GPU: weights (bf16 device tensors in pointer order),
-    a bf16 KV cache tensor, and the library handle with a loaded schedule."""
+    a bf16 KV cache tensor, and the library handle with a loaded schedule.
+    With ``batch`` > 1 the cache tensor holds every sequence's cache, one
+    after the other, and decoding goes through ``decode_batch``."""
 
     def __init__(self, cfg, weights: Sequence[torch.Tensor], kv_cache: torch.Tensor, max_seq: int,
-                 n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None):
+                 n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None, batch: int = 1):
         self.cfg = cfg
         self.ccfg = capi.make_config(cfg)
         self.weights = list(weights)
         self.kv = kv_cache
         self.max_seq = max_seq
+        self.batch = batch
         self.device = kv_cache.device.index if device is None else device
         for i, w in enumerate(self.weights):
             r, c = capi.mkd_weight_shape(self.ccfg, i)
@@ -27,9 +30,9 @@ class Decoder:
                 raise ValueError(f"weight {i}: expected contiguous bf16 with {r}x{c} elements")
         if kv_cache.dtype != torch.bfloat16 or not kv_cache.is_contiguous():
             raise ValueError("kv cache must be contiguous bf16")
-        if kv_cache.numel() * 2 != capi.mkd_kv_cache_bytes(self.ccfg, max_seq):
-            raise ValueError("kv cache size does not match max_seq")
-        self.handle = capi.mkd_init(self.ccfg, self.weights, kv_cache, max_seq, self.device)
+        if kv_cache.numel() * 2 != batch * capi.mkd_kv_cache_bytes(self.ccfg, max_seq):
+            raise ValueError("kv cache size does not match max_seq and batch")
+        self.handle = capi.mkd_init_batch(self.ccfg, self.weights, kv_cache, max_seq, batch, self.device)
         self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
 
     @property
@@ -64,6 +67,26 @@ class Decoder:
         if forced is not None:
             f = torch.tensor(list(forced), dtype=torch.int32, device=dev)
         self.launch(first_token, start_pos, n_steps, toks, logits, f)
+        capi.mkd_wait(self.handle, timeout_ms)
+        torch.cuda.synchronize(dev)
+        return toks, logits
+
+    def launch_batch(self, first_tokens: Sequence[int], start_pos: Sequence[int], n_steps: int,
+                     tokens_out: torch.Tensor, logits_out: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Enqueue one decode launch for every sequence (asynchronous)."""
+        if len(first_tokens) != self.batch or len(start_pos) != self.batch:
+            raise ValueError(f"need {self.batch} first tokens and start positions")
+        capi.mkd_decode_batch(self.handle, first_tokens, start_pos, n_steps, tokens_out, logits_out, stream)
+
+    def decode_batch(self, first_tokens: Sequence[int], start_pos: Sequence[int], n_steps: int,
+                     want_logits: bool = True, timeout_ms: int = 120000):
+        """Run one batched launch and wait: (tokens [B, n] int32, logits [B, n, V] float32 or None)."""
+        dev = self.kv.device
+        B = self.batch
+        toks = torch.empty(B, n_steps, dtype=torch.int32, device=dev)
+        logits = (torch.empty(B, n_steps, self.cfg.vocab, dtype=torch.float32, device=dev)
+                  if want_logits else None)
+        self.launch_batch(first_tokens, start_pos, n_steps, toks, logits)
         capi.mkd_wait(self.handle, timeout_ms)
         torch.cuda.synchronize(dev)
         return toks, logits

@@ -52,6 +52,17 @@ def run_bytes(cfg, start_pos: int, n_steps: int) -> int:
     return n_steps * w + kv * s
 
 
+def batch_run_bytes(cfg, start_positions, n_steps: int) -> int:
+    """Bytes of one launch decoding several sequences together for ``n_steps``
+    steps: each step reads every weight once for all of them (plus one
+    embedding row per sequence), and each sequence reads and appends its own
+    cache rows as in ``run_bytes``."""
+    B = len(start_positions)
+    w = weight_bytes_per_step(cfg) + (B - 1) * 2 * cfg.d_model
+    kv = sum(run_bytes(cfg, s, n_steps) - n_steps * weight_bytes_per_step(cfg) for s in start_positions)
+    return n_steps * w + kv
+
+
 def floor_seconds(n_bytes: float, bandwidth: float = HBM_PEAK_BYTES_PER_S) -> float:
     return n_bytes / bandwidth
 

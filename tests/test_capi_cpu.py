@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version():
-    assert capi.mkd_version() == 1
+    assert capi.mkd_version() == 2
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama1b", "llama3b", "mixtral"])
@@ -73,6 +73,55 @@ def test_schedule_bit_exact_with_oracle(name, n_wg):
         assert got.dtype == np.int32 and got.shape == want.shape
         assert np.array_equal(got, want)
         capi.mkd_schedule_validate(c, got)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b"])
+@pytest.mark.parametrize("batch", [2, 3, 8])
+def test_batched_schedule_bit_exact_with_oracle(name, batch):
+    cfg = synth.PRESETS[name]
+    c = capi.make_config(cfg)
+    for n_wg in (1, 7, 64, 256):
+        for n_chunks in (1, 4):
+            got = capi.mkd_schedule_build_batch(c, n_wg, n_chunks, batch)
+            want = S.build(cfg, n_wg, n_chunks, batch)
+            assert np.array_equal(got, want)
+            capi.mkd_schedule_validate(c, got)
+
+
+def test_batched_schedule_rejects_bad_batch_and_sequence_words():
+    cfg = synth.PRESETS["tiny"]
+    c = capi.make_config(cfg)
+    for batch in (0, 9):
+        with pytest.raises(capi.MkdError):
+            capi.mkd_schedule_build_batch(c, 8, 2, batch)
+    good = capi.mkd_schedule_build_batch(c, 8, 2, 3)
+    hdr, lists = S.parse(good)
+    body = good[S.WORDS + 8:].reshape(8, hdr[4], S.WORDS)
+    # an attention instruction naming a sequence past the batch
+    w, k = next((w, k) for w in range(8) for k in range(len(lists[w])) if lists[w][k][0] == S.OP_ATTN)
+    for bad_seq in (3, -1):
+        bad = good.copy()
+        bad[S.WORDS + 8 + (w * hdr[4] + k) * S.WORDS + 10] = bad_seq
+        with pytest.raises(ValueError):
+            S.validate(bad, cfg)
+        with pytest.raises(capi.MkdError):
+            capi.mkd_schedule_validate(c, bad)
+    # the header's batch changed: the attention stages no longer match
+    bad = good.copy()
+    bad[15] = 2
+    with pytest.raises(capi.MkdError):
+        capi.mkd_schedule_validate(c, bad)
+    assert body.shape[0] == 8
+
+
+def test_init_batch_rejects_batch_out_of_range_and_moe():
+    """Checked before any device call."""
+    for name, batch, code in (("tiny", 0, capi.MKD_E_INVALID), ("tiny", 9, capi.MKD_E_INVALID),
+                              ("tiny_moe", 2, capi.MKD_E_UNSUPPORTED)):
+        c = capi.make_config(synth.PRESETS[name])
+        with pytest.raises(capi.MkdError) as e:
+            capi.mkd_init_batch(c, [], None, 64, batch)
+        assert e.value.code == code
 
 
 def test_validator_rejects_mutations():

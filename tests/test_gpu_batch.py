@@ -1,0 +1,88 @@
+"""GPU parity of batched decode: B sequences decoded together in one launch
+(each weight row read once per step for all of them), each sequence checked
+against its own oracle run from its own cache and start position."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from persistent_megakernel_decode_02_amd import capi
+from persistent_megakernel_decode_02_amd.decoder import Decoder
+from tests.gpu_common import check_run, close_enough, oracle_run, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+STARTS = [40, 13, 77, 1, 0, 120, 31, 64]
+
+
+def _caches(cfg, max_seq, starts, device):
+    """One random-filled cache per sequence (its own seed), filled up to its start."""
+    return [synth.gen_kv_cache(cfg, max_seq, s, seed=synth.SEED_KV + 101 * b, device=device)
+            for b, s in enumerate(starts)]
+
+
+def _run_batched(cfg, starts, N, n_wg, n_chunks, gain_std):
+    B = len(starts)
+    max_seq = max(starts) + N
+    w_gpu = synth.gen_weights(cfg, device="cuda", gain_std=gain_std)
+    kv_gpu = torch.stack(_caches(cfg, max_seq, starts, "cuda")).contiguous()
+    kv0 = kv_gpu.clone()
+    firsts = synth.gen_tokens(B, cfg.vocab, stream=11)
+    say(f"{cfg.name} B={B} starts={starts} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B)
+    toks, logits = dec.decode_batch(firsts, starts, N)
+    toks2, logits2 = dec.decode_batch(firsts, starts, N)
+    assert torch.equal(toks, toks2) and torch.equal(logits, logits2), "two identical launches differ"
+    dec.close()
+    for b, s in enumerate(starts):
+        # positions before each sequence's start are left untouched
+        assert torch.equal(kv_gpu[b, :, :, :, :s], kv0[b, :, :, :, :s]), f"seq {b}: cache prefix changed"
+    out = (toks.cpu().numpy(), logits.cpu().numpy(), kv_gpu.float().cpu().numpy(), firsts, max_seq)
+    del w_gpu, kv_gpu, kv0
+    torch.cuda.empty_cache()
+    return out
+
+
+def _check_against_oracle(cfg, starts, N, res, gain_std):
+    toks, logits, kv_g, firsts, max_seq = res
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=gain_std)
+    for b, (s, kv_cpu) in enumerate(zip(starts, _caches(cfg, max_seq, starts, "cpu"))):
+        otoks, ologits, kv_o = oracle_run(cfg, w_cpu, kv_cpu, firsts[b], s, N)
+        check_run(f"{cfg.name} B={len(starts)} seq {b}", toks[b], logits[b], otoks, ologits)
+        ok, mx, _ = close_enough(kv_g[b][:, :, :, s:s + N], kv_o[:, :, :, s:s + N])
+        assert ok, f"seq {b}: appended kv max err {mx}"
+
+
+@pytest.mark.parametrize("B,n_wg,n_chunks", [(2, 256, 1), (3, 33, 2), (4, 64, 4), (5, 7, 3),
+                                             (8, 256, 1), (8, 40, 2)])
+def test_tiny_batched_kv_context(B, n_wg, n_chunks):
+    require_gpu()
+    cfg = synth.PRESETS["tiny"]
+    starts, N = STARTS[:B], 6
+    res = _run_batched(cfg, starts, N, n_wg, n_chunks, 0.1)
+    _check_against_oracle(cfg, starts, N, res, 0.1)
+
+
+def test_llama1b_batched_full_size():
+    """Four sequences at different cache lengths around 128 on the 1B shape."""
+    require_gpu()
+    cfg = synth.PRESETS["llama1b"]
+    starts, N = [128, 96, 131, 64], 3
+    res = _run_batched(cfg, starts, N, 0, 0, 0.0)
+    _check_against_oracle(cfg, starts, N, res, 0.0)
+
+
+def test_batched_handle_rejects_single_sequence_call():
+    require_gpu()
+    cfg = synth.PRESETS["tiny"]
+    w = synth.gen_weights(cfg, device="cuda")
+    kv = torch.stack(_caches(cfg, 64, [8, 8], "cuda")).contiguous()
+    dec = Decoder(cfg, w, kv, 64, batch=2)
+    toks = torch.empty(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(capi.MkdError):
+        capi.mkd_decode(dec.handle, 1, 8, 4, toks)
+    # a start position past the cache is rejected before launch
+    toks2 = torch.empty(2, 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(capi.MkdError):
+        capi.mkd_decode_batch(dec.handle, [1, 2], [8, 62], 4, toks2)
+    dec.close()

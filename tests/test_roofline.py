@@ -54,3 +54,15 @@ def test_moe_counts_only_routed_experts():
 def test_run_bytes_is_sum_of_steps(name, T0, n):
     cfg = synth.PRESETS[name]
     assert R.run_bytes(cfg, T0, n) == sum(R.step_bytes(cfg, T0 + i) for i in range(n))
+
+
+def test_batch_bytes_reduce_to_single_sequence_and_share_weights():
+    cfg = synth.PRESETS["llama1b"]
+    assert R.batch_run_bytes(cfg, [128], 7) == R.run_bytes(cfg, 128, 7)
+    kv = R.kv_bytes_per_position(cfg)
+    # four sequences: weights once per step, four embedding rows, four caches
+    got = R.batch_run_bytes(cfg, [128, 0, 5, 1000], 3)
+    want = 3 * (R.weight_bytes_per_step(cfg) + 3 * 2 * cfg.d_model)
+    for s in (128, 0, 5, 1000):
+        want += kv * sum(p + 2 for p in range(s, s + 3))
+    assert got == want

@@ -25,6 +25,30 @@ def test_simulator_no_deadlock_no_hazard(n_wg, n_chunks, start):
         S.simulate(cfg, w, n_tokens=3, seed=seed, start_pos=start)
 
 
+@pytest.mark.parametrize("batch", [2, 3, 8])
+def test_oracle_batched_schedule_valid(batch):
+    for name in ("tiny", "llama1b"):
+        cfg = synth.PRESETS[name]
+        for n_wg in (1, 5, 64, 256):
+            for n_chunks in (1, 4):
+                w = S.build(cfg, n_wg, n_chunks, batch)
+                S.validate(w, cfg)
+                hdr, lists = S.parse(w)
+                assert hdr[15] == batch
+                seqs = {ins[10] for lst in lists for ins in lst if ins[0] in (S.OP_ATTN, S.OP_AREDUCE)}
+                assert seqs == set(range(batch))
+                assert all(ins[10] == 0 for lst in lists for ins in lst if ins[0] in S.TILED_OPS)
+
+
+@pytest.mark.parametrize("n_wg,n_chunks,batch,starts", [(1, 1, 2, [0, 3]), (5, 2, 3, [7, 0, 20]),
+                                                         (16, 4, 4, [40, 2, 9, 33]), (3, 1, 8, list(range(8)))])
+def test_simulator_batched_no_deadlock_no_hazard(n_wg, n_chunks, batch, starts):
+    cfg = synth.PRESETS["tiny"]
+    w = S.build(cfg, n_wg, n_chunks, batch)
+    for seed in range(2):
+        S.simulate(cfg, w, n_tokens=2, seed=seed, start_pos=starts)
+
+
 def test_simulator_moe():
     from tests.test_oracle_pins import MICRO_MOE
     w = S.build(MICRO_MOE, 4, 2)
