@@ -179,8 +179,8 @@ def main() -> int:
     peak = roofline.HBM_PEAK_BYTES_PER_S
     floor_us = roofline.floor_seconds(n_bytes) * 1e6 / N
 
-    if args.trace and B == 1:
-        trace_breakdown(dec, first, T0, N)
+    if args.trace:
+        trace_breakdown(dec, one, N)
 
     cpu = None
     if args.cpu_sample > 0:
@@ -220,7 +220,7 @@ def main() -> int:
     return 0
 
 
-def trace_breakdown(dec, first, T0, N):
+def trace_breakdown(dec, launch_and_wait, N):
     """Per-opcode time from the device trace (one extra traced launch)."""
     import numpy as np
     import torch
@@ -229,9 +229,7 @@ def trace_breakdown(dec, first, T0, N):
     n_wg, max_instr = int(words[2]), int(words[4])
     tr = torch.zeros(n_wg * N * max_instr * 4, dtype=torch.int64, device="cuda")
     capi.mkd_set_trace(dec.handle, tr)
-    toks = torch.empty(N, dtype=torch.int32, device="cuda")
-    dec.launch(first, T0, N, toks)
-    capi.mkd_wait(dec.handle, 600000)
+    launch_and_wait()
     capi.mkd_set_trace(dec.handle, None)
     hz = capi.mkd_clock_hz(dec.handle)
     t = tr.cpu().numpy().reshape(n_wg, N, max_instr, 4)

@@ -264,6 +264,9 @@ static int out_floats_for(const mkd_config* c, int n_wg, int n_chunks, int batch
     if (s.op == OP_UPGATE || s.op == OP_MOE_UPGATE || s.op == OP_MOE_DOWN) rows *= 2;
     best = rows > best ? rows : best;
   }
+  // several sequences: plus the partial sums of tiles whose rows are split
+  // over K between wavefronts (fewer than 64 partial rows per tile)
+  if (batch > 1) best += 64;
   return ((best * batch) + 3) & ~3;
 }
 

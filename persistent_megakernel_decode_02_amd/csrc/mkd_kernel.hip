@@ -126,6 +126,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
+// Wavefront sums of four values at once.  Two values trade half-waves
+// (v_permlane32_swap) and are added, so one register holds the 32-lane
+// partial sums of both (lanes 0-31 the first, 32-63 the second); two such
+// registers trade 16-lane rows (v_permlane16_swap) and are added, so each
+// row holds the 16-lane partials of one value; a row reduction finishes.
+// Row r of the result holds the sum of v[kQuadValue[r]] in all its lanes.
+// (10 instructions for four sums, against 11 per sum with wave_sum.)
+constexpr int kQuadValue[4] = {0, 2, 1, 3};
+__device__ __forceinline__ float quad_sum(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+  const float u01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float u23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(u01), __float_as_uint(u23), false, false);
+  return sum16(__uint_as_float(c[0]) + __uint_as_float(c[1]));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            (int)kBufFlags);
@@ -509,9 +526,15 @@ __device__ __forceinline__ bool fetch_partials(Ctx& c, int tt) {
   return gather<1>(c, f, p.n_stages - 1, (uint32_t)(tt + 1), p.n_lm_tiles);
 }
 
-__shared__ int s_tok[kMaxBatch];  // every sequence's token of step sflag[2]
+// Every sequence's token of step sflag[2], kept at the end of the reduction
+// scratch (words kTokWord .. + kMaxBatch are used by nothing else).  A
+// static __shared__ array here instead moved the dynamic LDS area and cost
+// 2% of batch-1 decode time.
+constexpr int kTokWord = 240;
+static_assert(kTokWord + kMaxBatch <= kRed, "token words inside the reduction scratch");
+__device__ __forceinline__ int* step_tok(Ctx& c) { return (int*)(c.red + kTokWord); }
 
-// tokens consumed at step t by every sequence, into s_tok (computed once per
+// tokens consumed at step t by every sequence, into step_tok (computed once per
 // step and workgroup; workgroup 0 records the previous step's argmax)
 __device__ __forceinline__ bool step_tokens(Ctx& c) {
   CKParams& p = c.p;
@@ -519,7 +542,7 @@ __device__ __forceinline__ bool step_tokens(Ctx& c) {
   __syncthreads();  // every thread is done with the previous step's tokens
   if (c.t == 0) {
     if (c.tid == 0)
-      for (int b = 0; b < c.B; ++b) s_tok[b] = p.first_tok[b];
+      for (int b = 0; b < c.B; ++b) step_tok(c)[b] = p.first_tok[b];
   } else {
     // teacher forcing (one sequence): workgroup 0 still folds the argmax to record it
     const int f = p.forced ? uni(ld_i32(p.forced + c.t)) : -1;
@@ -529,15 +552,15 @@ __device__ __forceinline__ bool step_tokens(Ctx& c) {
         const int am = argmax_staged(c, b);
         if (c.tid == 0) {
           if (c.wg == 0) st_i32(p.tokens_out + (size_t)b * p.n_steps + c.t - 1, am);
-          if (f < 0) s_tok[b] = am;
+          if (f < 0) step_tok(c)[b] = am;
         }
       }
     }
-    if (f >= 0 && c.tid == 0) s_tok[0] = f;
+    if (f >= 0 && c.tid == 0) step_tok(c)[0] = f;
   }
   __syncthreads();
   bool bad = false;
-  for (int b = 0; b < c.B; ++b) bad = bad || s_tok[b] < 0 || s_tok[b] >= p.V;
+  for (int b = 0; b < c.B; ++b) bad = bad || step_tok(c)[b] < 0 || step_tok(c)[b] >= p.V;
   if (bad) {
     if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
     __syncthreads();
@@ -700,7 +723,7 @@ __device__ __forceinline__ bool embed_rows(Ctx& c, int r0, int r1, float* dst) {
   if (!step_tokens(c)) return false;
   const int B = c.B;
   for (int b = 0; b < B; ++b) {
-    const uint16_t* e = wptr(p, W_EMBED) + (size_t)s_tok[b] * p.d;
+    const uint16_t* e = wptr(p, W_EMBED) + (size_t)step_tok(c)[b] * p.d;
     for (int i = r0 + c.tid; i < r1; i += kThreads) dst[(i - r0) * B + b] = bf_val(ld_u16(e + i));
   }
   return true;
@@ -1128,9 +1151,10 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
 
 // ---------------------------------------------------------------- several sequences
 
-// xs[i * NB + b] <- rmsnorm of sequence b's vector (element i), times gamma[i]
+// xs[i * NB + b] <- rmsnorm of sequence b's vector (element i), times
+// gamma[i] (this thread's first gains already in registers)
 template <int NB>
-__device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma) {
+__device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma, const Gains& gr) {
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
@@ -1151,7 +1175,15 @@ __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma) 
     for (int w = 0; w < kWaves; ++w) tot += c.red[b * kWaves + w];
     inv[b] = 1.0f / sqrtf(tot / (float)d + c.p.eps);
   }
-  for (int i = c.tid; i < d; i += kThreads) {
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = c.tid + k * kThreads;
+    if (i < d) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) c.xs[i * NB + b] = (c.xs[i * NB + b] * inv[b]) * gr.g[k];
+    }
+  }
+  for (int i = c.tid + kGainRegs * kThreads; i < d; i += kThreads) {
     const float g = bf_val(ld_u16(gamma + i));
 #pragma unroll
     for (int b = 0; b < NB; ++b) c.xs[i * NB + b] = (c.xs[i * NB + b] * inv[b]) * g;
@@ -1162,50 +1194,82 @@ __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma) 
 // Rows of one instruction dotted with NB input vectors at once.  The inputs
 // sit interleaved in LDS (element k of sequence b at xs[k * NB + b]), so
 // the slice a lane needs for one 16-byte weight load (8 elements) is 8 NB
-// contiguous floats.  A wavefront takes its stream rows in groups of G and
-// walks a group segment by segment: each ring step holds the G rows' units
-// of one segment, and one read of the input slice serves all G of them
-// (LDS traffic per weight byte falls by G).  The ring is D steps deep (G D
-// units, 8 KiB per wavefront in flight).  Loads past the last row use
-// zero-size descriptors, so every refill is issued without a branch.
+// contiguous floats.  The workgroup's 8 wavefronts form a WR x WS grid over
+// the tile: wavefront (wr, ws) takes stream rows wr, wr + WR, ... and
+// segments ws, ws + WS, ...  A tile with many rows keeps whole rows per
+// wavefront (WS = 1); a tile with few rows (QKV, O-proj and down tiles are
+// 8-12 rows) also splits K, so that every wavefront still has rows to group
+// and loads to keep in flight, and the WS partial sums of a row are added in
+// LDS afterwards, in a fixed order.  A wavefront walks its rows in groups of
+// G, segment by segment: one ring step holds the G rows' units of one
+// segment, and one read of the input slice serves all G (LDS traffic per
+// weight byte falls G-fold).  The ring is D steps deep (12 KiB per
+// wavefront); DPRE steps are requested before the inputs are waited for
+// (all of them measured best: deeper rings and later refills were slower).
+// Loads past the wavefront's last row use zero-size descriptors, so every
+// refill is issued without a branch.
 template <int NB>
 struct BatchStream {
-  static constexpr int G = 4, D = 2;
-  const GenMap& m;
-  const int K, nseg, ns, steps;
+  static constexpr int G = 4, D = 3, DPRE = 3;
+  const GemvDesc& g;
+  const int K, nseg, ns;
+  int WR, WS, wr, ws, nrow, nsw, steps;
   const uint32_t lane16;
-  int pseg, pg;                     // producer: segment, group
+  int pg, pi;                       // producer: row group, segment (of this wavefront's)
   __amdgpu_buffer_rsrc_t pr[G];     // the producer group's row descriptors
   u32x4 ring[D][G];
 
-  __device__ __forceinline__ BatchStream(const GenMap& m_, int K_, int ns_, int lane)
-      : m(m_), K(uni(K_)), nseg(uni((K_ + 511) >> 9)), ns(uni(ns_)),
-        steps(uni(((ns_ + G - 1) / G) * ((K_ + 511) >> 9))), lane16((uint32_t)lane * 16u), pseg(0), pg(0) {
+  __device__ __forceinline__ BatchStream(const GemvDesc& g_, int ns_, int wave, int lane)
+      : g(g_), K(uni(g_.K)), nseg(uni((g_.K + 511) >> 9)), ns(uni(ns_)), lane16((uint32_t)lane * 16u),
+        pg(0), pi(0) {
+    WR = kWaves;
+    WS = 1;
+    while (WR > 1 && ns < 4 * WR && 2 * WS <= nseg) {
+      WR >>= 1;
+      WS <<= 1;
+    }
+    wr = wave / WS;
+    ws = wave % WS;
+    nrow = ns > wr ? (ns - wr + WR - 1) / WR : 0;
+    nsw = (nseg - ws + WS - 1) / WS;
+    steps = ((nrow + G - 1) / G) * nsw;
     set_group();
+  }
+  // stream row k of the tile: output row a + k (or a + k/2, gate or up)
+  __device__ __forceinline__ const uint16_t* row(int k) const {
+    return g.R == 2 ? row_of(g, g.a + (k >> 1), k & 1) : row_of(g, g.a + k, 0);
   }
   __device__ __forceinline__ void set_group() {
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      const int k = pg * G + r;
-      const bool live = k < ns;
-      pr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(m.row(live ? k : 0)), (short)0,
+      const int i = pg * G + r;
+      const bool live = i < nrow;
+      pr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row(live ? wr + i * WR : 0)), (short)0,
                                                 live ? 2 * K : 0, (int)kBufFlags);
     }
   }
   __device__ __forceinline__ void issue(u32x4 (&dst)[G]) {
+    const int seg = ws + pi * WS;
 #pragma unroll
     for (int r = 0; r < G; ++r)
-      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(pr[r], (int)lane16, pseg * 1024, kNT);
-    if (++pseg == nseg) {
-      pseg = 0;
+      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(pr[r], (int)lane16, seg * 1024, kNT);
+    if (++pi == nsw) {
+      pi = 0;
       ++pg;
       set_group();
     }
   }
   __device__ __forceinline__ void prefetch() {
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(ring[d]);
+    for (int d = 0; d < DPRE; ++d) issue(ring[d]);
   }
+  // after the inputs have arrived
+  __device__ __forceinline__ void prefetch_rest() {
+#pragma unroll
+    for (int d = DPRE; d < D; ++d) issue(ring[d]);
+  }
+  // Row results: out[k * NB + b] when WS == 1, else this wavefront's partial
+  // at out[(ns + ws * ns + k) * NB + b] (combine() adds them up).
   __device__ __forceinline__ void run(const float* xs, float* out) {
     const float* xl = xs + lane16 / 16u * 8 * NB;
     float acc[G][NB];
@@ -1213,9 +1277,10 @@ struct BatchStream {
     for (int r = 0; r < G; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-    int cseg = 0, cg = 0;
+    int ci = 0, cg = 0;
+    float* const dst = WS == 1 ? out : out + (size_t)(ns + ws * ns) * NB;
     auto eat = [&](const u32x4 (&w)[G]) {
-      const f32x4* xp = (const f32x4*)(xl + cseg * 512 * NB);
+      const f32x4* xp = (const f32x4*)(xl + (ws + ci * WS) * 512 * NB);
       float x[8 * NB];
 #pragma unroll
       for (int q = 0; q < 2 * NB; ++q) {
@@ -1224,27 +1289,33 @@ struct BatchStream {
       }
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        const uint32_t wr[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+        const uint32_t wv[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float wj = (j & 1) ? bf_hi(wr[j >> 1]) : bf_lo(wr[j >> 1]);
+          const float wj = (j & 1) ? bf_hi(wv[j >> 1]) : bf_lo(wv[j >> 1]);
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[r][b] = fmaf(wj, x[j * NB + b], acc[r][b]);
         }
       }
-      if (++cseg == nseg) {
+      if (++ci == nsw) {
+        // the G x NB sums, four at a time; the first lane of row rr holds
+        // value 4q + kQuadValue[rr] of the group (row-major over (row, sequence))
+        const int rr = (int)(lane16 >> 8);
+        const bool writer = ((lane16 >> 4) & 15u) == 0;
 #pragma unroll
-        for (int r = 0; r < G; ++r) {
-          const int k = cg * G + r;
-          const int o = m.slot(k) * NB;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const float v = wave_sum(acc[r][b]);
-            if (k < ns) out[o + b] = v;
-            acc[r][b] = 0.f;
-          }
+        for (int q = 0; q < G * NB / 4; ++q) {
+          const float v = quad_sum(acc[(4 * q) / NB][(4 * q) % NB], acc[(4 * q + 1) / NB][(4 * q + 1) % NB],
+                                   acc[(4 * q + 2) / NB][(4 * q + 2) % NB], acc[(4 * q + 3) / NB][(4 * q + 3) % NB]);
+          const int vi = 4 * q + (rr == 1 ? 2 : (rr == 2 ? 1 : rr));
+          const int r = vi / NB, bq = vi - r * NB;
+          const int i = cg * G + r;
+          if (writer && i < nrow) dst[(wr + i * WR) * NB + bq] = v;
         }
-        cseg = 0;
+#pragma unroll
+        for (int r = 0; r < G; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+        ci = 0;
         ++cg;
       }
     };
@@ -1262,6 +1333,16 @@ struct BatchStream {
       }
     }
   }
+  // out[j] = sum over the WS segment groups of their partials (after a barrier)
+  __device__ __forceinline__ void combine(Ctx& c, float* out) const {
+    if (WS == 1) return;
+    for (int j = c.tid; j < ns * NB; j += kThreads) {
+      float v = 0.f;
+      for (int q = 0; q < WS; ++q) v += out[(size_t)(ns + q * ns) * NB + j];
+      out[j] = v;
+    }
+    __syncthreads();
+  }
 };
 
 // One dense GEMV instruction for NB sequences: the same rows, inputs and
@@ -1275,14 +1356,19 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   const uint16_t* gamma;
   bool embed_x, embed_res;
   gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
-  const GenMap m{g};
-  BatchStream<NB> bs(m, g.K, g.R * wave_rows(b - a, c.wave), c.lane);
+  BatchStream<NB> bs(g, g.R * (b - a), c.wave, c.lane);
   bs.prefetch();
+  const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
   if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
-  if (gamma) rmsnorm_b<NB>(c, p.d, gamma);
+  // everything requested so far has arrived (loads complete in order);
+  // saying so keeps the waits of the row loop exact
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  bs.prefetch_rest();
+  if (gamma) rmsnorm_b<NB>(c, p.d, gamma, gr);
   bs.run(c.xs, c.out);
   mark_computed(c);
   __syncthreads();
+  bs.combine(c, c.out);
   gemv_epilogue<NB>(c, op, l, a, b, index, tag);
   return true;
 }
