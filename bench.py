@@ -37,10 +37,11 @@ def kernel_digest() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload_key: str):
+def measured_traffic(kernel: str, workload_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"mkd_megakernel_{workload_key}_traffic.json")
+    this kernel and workload, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_key}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
@@ -187,7 +188,8 @@ def main() -> int:
         cpu = cpu_baseline(cfg, T0, args.cpu_sample, first)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
     key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
-    traffic = measured_traffic(key)
+    kernel = "mkd_megakernel" if B == 1 else "mkd_megakernel_batch"
+    traffic = measured_traffic(kernel, key)
     out = {
         "metric": "batch-1 decode tokens/s" if B == 1 else f"batch-{B} decode tokens/s",
         "value": B * N * args.steps / wall,
@@ -210,7 +212,7 @@ def main() -> int:
         "roofline_us_per_token": floor_us,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "mkd_megakernel" if B == 1 else "mkd_megakernel_batch",
+                     "kernel": kernel,
                      "algorithmic_bytes_per_launch": n_bytes,
                      "kernel_ms_mean": kernel_s * 1e3},
         "cpu_baseline": cpu,
