@@ -309,15 +309,20 @@ static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max) {
 
 static int32_t round16i(int64_t n) { return (int32_t)((n + 15) / 16 * 16); }
 
-static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch) {
+// LDS floats for the staged input vectors (and the other staging uses of
+// that area); with_act false leaves out the down projection's input, which
+// several sequences may stream in passes over K (one segment at least)
+static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch, bool with_act = true) {
   const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
   const int qd = c->n_q_heads * hd;
   auto pad = [](int n) { return (n + 511) & ~511; };   // streamer rows read x in 512-wide segments
-  int x = pad(c->d_model);
-  x = x > pad(qd) ? x : pad(qd);
-  const int act = pad(c->d_ff) * (c->top_k ? c->top_k : 1);
+  // one input vector per sequence, interleaved; with several sequences every
+  // 8-element slice (8 * batch floats) is followed by 4 padding floats
+  auto vec = [&](int n) { return batch == 1 ? pad(n) : pad(n) / 8 * (8 * batch + 4); };
+  int x = vec(c->d_model);
+  x = x > vec(qd) ? x : vec(qd);
+  const int act = with_act ? vec(c->d_ff) * (c->top_k ? c->top_k : 1) : vec(512);
   x = x > act ? x : act;
-  x *= batch;                                           // one input vector per sequence
   const int lm = 2 * n_lm * batch;                      // every sequence's LM-head partials
   x = x > lm ? x : lm;
   const int ared = n_chunks * (hd + 2);
@@ -325,6 +330,31 @@ static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch) 
   const int attn = (G + 2) * hd + kWaves * G * (hd + 2);
   x = x > attn ? x : attn;
   return (x + 3) & ~3;
+}
+
+constexpr size_t kLdsSlack = 256;  // static LDS of the kernel and a margin
+
+// Several sequences: when the interleaved down-projection input does not fit
+// in LDS next to everything else, shrink the input area to what fits, in
+// whole 512-element segments per sequence; the down projection then runs in
+// passes over K.  The other inputs (normalised as a whole) are never split:
+// if even they do not fit, the area is left as is and the LDS check fails.
+// MKD_BATCH_X_FLOATS caps the area further (within the same bounds), so that
+// the passes can be exercised on small models.
+static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int batch, int lds_max) {
+  if (batch == 1) return;
+  if (const char* e = getenv("MKD_BATCH_X_FLOATS")) {
+    const int seg = 64 * (8 * batch + 4);   // one 512-element segment of every sequence, padded
+    const int cap = atoi(e) / seg * seg;
+    if (cap > 0 && cap < p.x_floats && cap >= x_floats_for(c, n_chunks, n_lm, batch, false)) p.x_floats = cap;
+  }
+  if (lds_max <= 0 || lds_bytes(p) + kLdsSlack <= (size_t)lds_max) return;
+  const size_t other = lds_bytes(p) - (size_t)p.x_floats * sizeof(float);
+  if (other + kLdsSlack >= (size_t)lds_max) return;
+  int x = (int)(((size_t)lds_max - kLdsSlack - other) / sizeof(float));
+  const int seg = 64 * (8 * batch + 4);
+  x = x / seg * seg;
+  if (x >= x_floats_for(c, n_chunks, n_lm, batch, false)) p.x_floats = x;
 }
 
 int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
@@ -339,6 +369,7 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
     p.d = m->cfg.d_model;
     int lds_max = 0;
     hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
+    fit_x(p, &m->cfg, 1, n_lm, m->batch, lds_max);
     p.pre_units = m->batch == 1 ? pre_units_for(&m->cfg, lds_bytes(p), lds_max) : 0;
     int mx = 0;
     const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, &mx);
@@ -367,6 +398,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   p.d = c->d_model;
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
+  fit_x(p, c, n_chunks, n_lm, batch, lds_max);
   p.pre_units = batch == 1 ? pre_units_for(c, lds_bytes(p), lds_max) : 0;
   const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
@@ -435,7 +467,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   m->n_chunks = n_chunks;
   m->max_instr = words[H_MAXINSTR];
   m->n_lm = n_lm;
-  m->x_floats = x_floats;
+  m->x_floats = p.x_floats;
   m->out_floats = out_floats;
   m->res_floats = res_floats;
   m->pre_units = p.pre_units;

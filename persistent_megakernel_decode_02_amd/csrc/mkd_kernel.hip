@@ -239,19 +239,37 @@ __device__ __forceinline__ void ll_issue(Ctx& c, const Span& sp, int base, Stage
     st.v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (base + k * kThreads + c.tid) * 16, 0, kSC1);
 }
 
-template <int S>
+// Where word i of a fetch lands in its LDS destination: in place, or (input
+// vectors of several sequences) in 8 NB-word slices padded by 4 words (SlicePad).
+struct InPlace {
+  __device__ __forceinline__ int operator()(int i) const { return i; }
+};
+// The input vectors of NB sequences, interleaved (element k of sequence b is
+// word k NB + b), are read by the batched GEMV one 8-element slice per lane:
+// 8 NB consecutive floats.  Unpadded, lane l's slice starts at 32 NB l bytes,
+// so 16 consecutive lanes fall on as few as one 16-byte bank group of LDS
+// (NB = 8) and every slice read is serialised.  Each slice is followed by 4
+// padding floats: lane l then starts at bank group (2 NB + 1) l mod 16, odd
+// times l, which is a different group for each of 16 consecutive lanes.
+template <int NB>
+struct SlicePad {
+  static constexpr int kStride = 8 * NB + 4;  // floats from one slice to the next
+  __device__ __forceinline__ int operator()(int i) const { return i + (i / (8 * NB)) * 4; }
+};
+
+template <int S, class M = InPlace>
 __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, const Staged<S>& st, int n,
-                                          uint32_t tag, float* dst) {
+                                          uint32_t tag, float* dst, M m = M()) {
   unsigned pending = 0;
 #pragma unroll
   for (int k = 0; k < S; ++k) {
     const int i0 = 2 * (base + k * kThreads + c.tid) - sp.lead;
     if (i0 >= 0 && i0 < n) {
-      if (st.v[k].y == tag) dst[i0] = __uint_as_float(st.v[k].x);
+      if (st.v[k].y == tag) dst[m(i0)] = __uint_as_float(st.v[k].x);
       else pending |= 1u << (2 * k);
     }
     if (i0 + 1 >= 0 && i0 + 1 < n) {
-      if (st.v[k].w == tag) dst[i0 + 1] = __uint_as_float(st.v[k].z);
+      if (st.v[k].w == tag) dst[m(i0 + 1)] = __uint_as_float(st.v[k].z);
       else pending |= 2u << (2 * k);
     }
   }
@@ -265,7 +283,7 @@ __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, cons
         const int wi = 2 * (base + (b >> 1) * kThreads + c.tid) + (b & 1);  // word of the span
         const uint64_t w = ll_load(sp.w0 + wi);
         if ((uint32_t)(w >> 32) == tag) {
-          dst[wi - sp.lead] = __uint_as_float((uint32_t)w);
+          dst[m(wi - sp.lead)] = __uint_as_float((uint32_t)w);
           pending &= ~(1u << b);
         }
       }
@@ -289,19 +307,20 @@ __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, cons
 }
 
 // batches of one fetch from pair `from` on, S loads per thread each
-template <int S>
+template <int S, class M = InPlace>
 __device__ __forceinline__ void ll_fetch_from(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst,
-                                              int from) {
+                                              int from, M m = M()) {
   const Span sp = span_of(src, n);
   for (int base = from; base < sp.npairs; base += S * kThreads) {
     Staged<S> st;
     ll_issue<S>(c, sp, base, st);
-    ll_finish<S>(c, sp, base, st, n, tag, dst);
+    ll_finish<S, M>(c, sp, base, st, n, tag, dst, m);
   }
 }
 
-__device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
-  ll_fetch_from<8>(c, src, n, tag, dst, 0);
+template <class M = InPlace>
+__device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst, M m = M()) {
+  ll_fetch_from<8, M>(c, src, n, tag, dst, 0, m);
 }
 
 // workgroup barrier; false when the launch is being aborted
@@ -414,8 +433,10 @@ struct Fetch {
 // The first batch of up to three fetches is issued before any is checked, so
 // one round trip covers an instruction's inputs (8192 words of the first,
 // 2048 of the others); longer inputs take further batches.
-template <int K>
-__device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count) {
+// (the first fetch's words land in its destination through m)
+template <int K, class M = InPlace>
+__device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count,
+                                       M m = M()) {
   constexpr int S0 = 8, S1 = 2;
   if (!wait_counter(c, stage, step_plus1, count)) return false;
   Staged<S0> st0;
@@ -431,10 +452,10 @@ __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, u
     sp2 = span_of(f[2].src, f[2].n);
     ll_issue<S1>(c, sp2, 0, st2);
   }
-  ll_finish<S0>(c, sp0, 0, st0, f[0].n, f[0].tag, f[0].dst);
+  ll_finish<S0, M>(c, sp0, 0, st0, f[0].n, f[0].tag, f[0].dst, m);
   if (K > 1) ll_finish<S1>(c, sp1, 0, st1, f[1].n, f[1].tag, f[1].dst);
   if (K > 2) ll_finish<S1>(c, sp2, 0, st2, f[2].n, f[2].tag, f[2].dst);
-  ll_fetch_from<S0>(c, f[0].src, f[0].n, f[0].tag, f[0].dst, S0 * kThreads);
+  ll_fetch_from<S0, M>(c, f[0].src, f[0].n, f[0].tag, f[0].dst, S0 * kThreads, m);
   if (K > 1) ll_fetch_from<S1>(c, f[1].src, f[1].n, f[1].tag, f[1].dst, S1 * kThreads);
   if (K > 2) ll_fetch_from<S1>(c, f[2].src, f[2].n, f[2].tag, f[2].dst, S1 * kThreads);
 #pragma unroll
@@ -444,9 +465,9 @@ __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, u
   return true;
 }
 
-template <int K>
-__device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K]) {
-  return gather<K>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count);
+template <int K, class M = InPlace>
+__device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K], M m = M()) {
+  return gather<K, M>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count, m);
 }
 
 // RMSNorm gains of this thread's elements (i = tid + k * kThreads), read
@@ -717,14 +738,15 @@ struct GenMap {
 constexpr int kNoSplit = 0x7fffffff;
 
 // the embedding rows [r0, r1) of every sequence's token of this step, into
-// dst interleaved (row r of sequence b at dst[(r - r0) * B + b])
-__device__ __forceinline__ bool embed_rows(Ctx& c, int r0, int r1, float* dst) {
+// dst interleaved (row r of sequence b at dst[m((r - r0) * B + b)])
+template <class M = InPlace>
+__device__ __forceinline__ bool embed_rows(Ctx& c, int r0, int r1, float* dst, M m = M()) {
   CKParams& p = c.p;
   if (!step_tokens(c)) return false;
   const int B = c.B;
   for (int b = 0; b < B; ++b) {
     const uint16_t* e = wptr(p, W_EMBED) + (size_t)step_tok(c)[b] * p.d;
-    for (int i = r0 + c.tid; i < r1; i += kThreads) dst[(i - r0) * B + b] = bf_val(ld_u16(e + i));
+    for (int i = r0 + c.tid; i < r1; i += kThreads) dst[m((i - r0) * B + b)] = bf_val(ld_u16(e + i));
   }
   return true;
 }
@@ -877,25 +899,26 @@ __device__ __forceinline__ void gemv_setup(Ctx& c, int op, int l, int a, int b, 
   }
 }
 
-// stage the instruction's input vectors in LDS (xs, and the residual rows in
-// res), every sequence's interleaved; xs is zero from K up to the next
-// multiple of 512 (the streamers read whole 512-element segments)
+// stage the instruction's input vectors in LDS (xs, word i at xs[m(i)], and
+// the residual rows in res), every sequence's interleaved; xs is zero from K
+// up to the next multiple of 512 (the streamers read whole 512-element segments)
+template <class M = InPlace>
 __device__ __forceinline__ bool gemv_inputs(Ctx& c, int a, int b, int K, const Fetch (&f)[2], bool embed_x,
-                                            bool embed_res) {
+                                            bool embed_res, M m = M()) {
   CKParams& p = c.p;
   if (embed_x) {
     // the token comes from the previous step's LM-head partials (it waits on
     // them itself); the embedding row is a plain read
-    if (!embed_rows(c, 0, p.d, c.xs)) return false;
+    if (!embed_rows(c, 0, p.d, c.xs, m)) return false;
     mark_ready(c);
     __syncthreads();
   } else {
     if (embed_res && !embed_rows(c, a, b, c.res)) return false;
-    if (!gather_inputs<2>(c, f)) return false;
+    if (!gather_inputs<2, M>(c, f, m)) return false;
   }
   if (K & 511) {
     const int B = c.B;
-    for (int i = K * B + c.tid; i < ((K + 511) & ~511) * B; i += kThreads) c.xs[i] = 0.f;
+    for (int i = K * B + c.tid; i < ((K + 511) & ~511) * B; i += kThreads) c.xs[m(i)] = 0.f;
     __syncthreads();
   }
   return true;
@@ -1151,16 +1174,17 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
 
 // ---------------------------------------------------------------- several sequences
 
-// xs[i * NB + b] <- rmsnorm of sequence b's vector (element i), times
-// gamma[i] (this thread's first gains already in registers)
+// sequence b's vector (element i at xs[SlicePad(i * NB + b)]) <- its
+// rmsnorm times gamma[i] (this thread's first gains already in registers)
 template <int NB>
 __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma, const Gains& gr) {
+  const SlicePad<NB> m;
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
   for (int i = c.tid; i < d; i += kThreads)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) ss[b] = fmaf(c.xs[i * NB + b], c.xs[i * NB + b], ss[b]);
+    for (int b = 0; b < NB; ++b) ss[b] = fmaf(c.xs[m(i * NB + b)], c.xs[m(i * NB + b)], ss[b]);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const float w = wave_sum(ss[b]);
@@ -1180,21 +1204,21 @@ __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma, 
     const int i = c.tid + k * kThreads;
     if (i < d) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) c.xs[i * NB + b] = (c.xs[i * NB + b] * inv[b]) * gr.g[k];
+      for (int b = 0; b < NB; ++b) c.xs[m(i * NB + b)] = (c.xs[m(i * NB + b)] * inv[b]) * gr.g[k];
     }
   }
   for (int i = c.tid + kGainRegs * kThreads; i < d; i += kThreads) {
     const float g = bf_val(ld_u16(gamma + i));
 #pragma unroll
-    for (int b = 0; b < NB; ++b) c.xs[i * NB + b] = (c.xs[i * NB + b] * inv[b]) * g;
+    for (int b = 0; b < NB; ++b) c.xs[m(i * NB + b)] = (c.xs[m(i * NB + b)] * inv[b]) * g;
   }
   __syncthreads();
 }
 
 // Rows of one instruction dotted with NB input vectors at once.  The inputs
-// sit interleaved in LDS (element k of sequence b at xs[k * NB + b]), so
-// the slice a lane needs for one 16-byte weight load (8 elements) is 8 NB
-// contiguous floats.  The workgroup's 8 wavefronts form a WR x WS grid over
+// sit interleaved in LDS (element k of sequence b at xs[SlicePad(k NB + b)]),
+// so the slice a lane needs for one 16-byte weight load (8 elements) is 8 NB
+// contiguous floats, and consecutive lanes' slices start on different banks.  The workgroup's 8 wavefronts form a WR x WS grid over
 // the tile: wavefront (wr, ws) takes stream rows wr, wr + WR, ... and
 // segments ws, ws + WS, ...  A tile with many rows keeps whole rows per
 // wavefront (WS = 1); a tile with few rows (QKV, O-proj and down tiles are
@@ -1219,9 +1243,13 @@ struct BatchStream {
   __amdgpu_buffer_rsrc_t pr[G];     // the producer group's row descriptors
   u32x4 ring[D][G];
 
-  __device__ __forceinline__ BatchStream(const GemvDesc& g_, int ns_, int wave, int lane)
+  // Segments [s0, s1) of every row (one pass; the input slice of segment s
+  // is at xs + (s - s0) * 512 NB).  The wavefront grid depends on the whole
+  // row length, so every pass of an instruction splits the work alike.
+  const int s0;
+  __device__ __forceinline__ BatchStream(const GemvDesc& g_, int ns_, int wave, int lane, int s0_, int s1_)
       : g(g_), K(uni(g_.K)), nseg(uni((g_.K + 511) >> 9)), ns(uni(ns_)), lane16((uint32_t)lane * 16u),
-        pg(0), pi(0) {
+        pg(0), pi(0), s0(uni(s0_)) {
     WR = kWaves;
     WS = 1;
     while (WR > 1 && ns < 4 * WR && 2 * WS <= nseg) {
@@ -1231,7 +1259,8 @@ struct BatchStream {
     wr = wave / WS;
     ws = wave % WS;
     nrow = ns > wr ? (ns - wr + WR - 1) / WR : 0;
-    nsw = (nseg - ws + WS - 1) / WS;
+    const int span = uni(s1_) - s0;
+    nsw = span > ws ? (span - ws + WS - 1) / WS : 0;
     steps = ((nrow + G - 1) / G) * nsw;
     set_group();
   }
@@ -1249,7 +1278,7 @@ struct BatchStream {
     }
   }
   __device__ __forceinline__ void issue(u32x4 (&dst)[G]) {
-    const int seg = ws + pi * WS;
+    const int seg = s0 + ws + pi * WS;
 #pragma unroll
     for (int r = 0; r < G; ++r)
       dst[r] = __builtin_amdgcn_raw_buffer_load_b128(pr[r], (int)lane16, seg * 1024, kNT);
@@ -1269,9 +1298,11 @@ struct BatchStream {
     for (int d = DPRE; d < D; ++d) issue(ring[d]);
   }
   // Row results: out[k * NB + b] when WS == 1, else this wavefront's partial
-  // at out[(ns + ws * ns + k) * NB + b] (combine() adds them up).
-  __device__ __forceinline__ void run(const float* xs, float* out) {
-    const float* xl = xs + lane16 / 16u * 8 * NB;
+  // at out[(ns + ws * ns + k) * NB + b] (combine() adds them up); a pass after
+  // the first adds to what the earlier passes left there.
+  __device__ __forceinline__ void run(const float* xs, float* out, bool add) {
+    constexpr int XS = SlicePad<NB>::kStride;
+    const float* xl = xs + lane16 / 16u * XS;   // this lane's slice of segment s0
     float acc[G][NB];
 #pragma unroll
     for (int r = 0; r < G; ++r)
@@ -1279,8 +1310,14 @@ struct BatchStream {
       for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
     int ci = 0, cg = 0;
     float* const dst = WS == 1 ? out : out + (size_t)(ns + ws * ns) * NB;
+    if (nsw == 0 && !add) {
+      // a first pass with no segment for this wavefront: its rows' sums start at zero
+      for (int i = 0; i < nrow; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dst[(wr + i * WR) * NB + b] = 0.f;
+    }
     auto eat = [&](const u32x4 (&w)[G]) {
-      const f32x4* xp = (const f32x4*)(xl + (ws + ci * WS) * 512 * NB);
+      const f32x4* xp = (const f32x4*)(xl + (ws + ci * WS) * 64 * XS);
       float x[8 * NB];
 #pragma unroll
       for (int q = 0; q < 2 * NB; ++q) {
@@ -1309,7 +1346,10 @@ struct BatchStream {
           const int vi = 4 * q + (rr == 1 ? 2 : (rr == 2 ? 1 : rr));
           const int r = vi / NB, bq = vi - r * NB;
           const int i = cg * G + r;
-          if (writer && i < nrow) dst[(wr + i * WR) * NB + bq] = v;
+          if (writer && i < nrow) {
+            float* o = dst + (wr + i * WR) * NB + bq;
+            *o = add ? *o + v : v;
+          }
         }
 #pragma unroll
         for (int r = 0; r < G; ++r)
@@ -1356,16 +1396,44 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   const uint16_t* gamma;
   bool embed_x, embed_res;
   gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
-  BatchStream<NB> bs(g, g.R * (b - a), c.wave, c.lane);
+  // The input vectors of all NB sequences must sit in LDS at once.  When
+  // they do not fit (the down projection's d_ff-long input at large NB), the
+  // row stream runs in passes over K, each with its slice of the inputs.
+  const int nseg = (g.K + 511) >> 9;
+  const SlicePad<NB> xm;
+  const int pseg = uni(min(nseg, p.x_floats / (64 * SlicePad<NB>::kStride)));   // segments per pass
+  const int ns = g.R * (b - a);
+  if (pseg < nseg && (gamma || embed_x)) {
+    // RMSNorm needs the whole vector at once; the host sizes the input area
+    // so that only the down projection's input is ever split
+    if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
+    return false;
+  }
+  const int k1 = min(g.K, pseg * 512);
+  f[0].n = k1 * NB;
+  BatchStream<NB> bs(g, ns, c.wave, c.lane, 0, pseg);
   bs.prefetch();
   const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
-  if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
+  if (!gemv_inputs(c, a, b, k1, f, embed_x, embed_res, xm)) return false;
   // everything requested so far has arrived (loads complete in order);
   // saying so keeps the waits of the row loop exact
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   bs.prefetch_rest();
   if (gamma) rmsnorm_b<NB>(c, p.d, gamma, gr);
-  bs.run(c.xs, c.out);
+  bs.run(c.xs, c.out, false);
+  for (int sa = pseg; sa < nseg; sa += pseg) {
+    const int sb = min(nseg, sa + pseg);
+    const int ka = sa * 512, kb = min(g.K, sb * 512);
+    BatchStream<NB> next(g, ns, c.wave, c.lane, sa, sb);
+    next.prefetch();
+    __syncthreads();  // every wavefront is done with the previous slice
+    ll_fetch(c, f[0].src + (size_t)ka * NB, (kb - ka) * NB, tag, c.xs, xm);
+    for (int i = (kb - ka) * NB + c.tid; i < (sb - sa) * 512 * NB; i += kThreads) c.xs[xm(i)] = 0.f;
+    if (!sync_ok(c)) return false;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    next.prefetch_rest();
+    next.run(c.xs, c.out, true);
+  }
   mark_computed(c);
   __syncthreads();
   bs.combine(c, c.out);

@@ -63,6 +63,29 @@ def test_tiny_batched_kv_context(B, n_wg, n_chunks):
     _check_against_oracle(cfg, starts, N, res, 0.1)
 
 
+@pytest.mark.parametrize("B,n_wg,n_chunks", [(3, 33, 2), (8, 256, 1)])
+def test_tiny_batched_down_projection_in_passes(B, n_wg, n_chunks, monkeypatch):
+    """The LDS input area capped to one 512-element segment of every sequence: the
+    down projection (d_ff 768) then streams its rows in two passes over K,
+    the second ragged, adding to the first pass's partial sums."""
+    require_gpu()
+    monkeypatch.setenv("MKD_BATCH_X_FLOATS", str(64 * (8 * B + 4)))
+    cfg = synth.PRESETS["tiny"]
+    starts, N = STARTS[:B], 5
+    res = _run_batched(cfg, starts, N, n_wg, n_chunks, 0.1)
+    _check_against_oracle(cfg, starts, N, res, 0.1)
+
+
+def test_llama1b_batched_full_size_b8():
+    """Eight sequences on the 1B shape: the interleaved down-projection input
+    (8192 x 8 floats) does not fit in LDS, so it streams in passes over K."""
+    require_gpu()
+    cfg = synth.PRESETS["llama1b"]
+    starts, N = [128, 96, 131, 64, 1, 200, 128, 17], 2
+    res = _run_batched(cfg, starts, N, 0, 0, 0.0)
+    _check_against_oracle(cfg, starts, N, res, 0.0)
+
+
 def test_llama1b_batched_full_size():
     """Four sequences at different cache lengths around 128 on the 1B shape."""
     require_gpu()
