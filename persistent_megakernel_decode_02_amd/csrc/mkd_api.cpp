@@ -488,17 +488,12 @@ int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks, int32_t* ho
   if (n_wg == 0) n_wg = m->n_cu;
   if (n_chunks == 0) {
     // one chunk (one attention instruction per q head) up to 512 KiB of K and
-    // V per head at max_seq, 16 up to 2 MiB, then one chunk per spare
-    // workgroup (at most 64)
+    // V per head at max_seq, else one chunk per workgroup and kv head (at
+    // most 64); measured best on the 1B and 3B shapes at KV 1024-16384
     const double head_bytes = (double)m->max_seq * m->cfg.head_dim * 4.0;  // K and V rows
     int cap = n_wg / m->cfg.n_kv_heads;
     cap = cap < 1 ? 1 : (cap > 64 ? 64 : cap);
-    if (head_bytes <= 512.0 * 1024)
-      n_chunks = 1;
-    else if (head_bytes <= 2.0 * 1024 * 1024)
-      n_chunks = cap < 16 ? cap : 16;
-    else
-      n_chunks = cap;
+    n_chunks = head_bytes <= 512.0 * 1024 ? 1 : cap;
   }
   size_t n = 0;
   int rc = mkd_schedule_build_batch(&m->cfg, n_wg, n_chunks, m->batch, nullptr, 0, &n);
