@@ -188,7 +188,7 @@ def main() -> int:
         cpu = cpu_baseline(cfg, T0, args.cpu_sample, first)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
     key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
-    kernel = "mkd_megakernel" if B == 1 else "mkd_megakernel_batch"
+    kernel = "mkd_megakernel_batch" if B > 1 else ("mkd_megakernel_moe" if cfg.is_moe else "mkd_megakernel")
     traffic = measured_traffic(kernel, key)
     out = {
         "metric": "batch-1 decode tokens/s" if B == 1 else f"batch-{B} decode tokens/s",

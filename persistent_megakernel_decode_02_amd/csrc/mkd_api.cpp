@@ -372,7 +372,7 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
     fit_x(p, &m->cfg, 1, n_lm, m->batch, lds_max);
     p.pre_units = m->batch == 1 ? pre_units_for(&m->cfg, lds_bytes(p), lds_max) : 0;
     int mx = 0;
-    const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, &mx);
+    const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, m->cfg.n_experts > 0, &mx);
     if (rc) return fail(rc, "occupancy query failed");
     *max_coop_wg = mx;
   }
@@ -405,7 +405,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
                                        std::to_string(lds_max) + " (use more workgroups)");
   int mx = 0;
-  int rc = max_coop_blocks(m->device, lds, batch, &mx);
+  int rc = max_coop_blocks(m->device, lds, batch, c->n_experts > 0, &mx);
   if (rc) return fail(rc, "occupancy query failed");
   if (n_wg > mx)
     return fail(MKD_E_COOPERATIVE, "n_wg " + std::to_string(n_wg) + " exceeds the " +

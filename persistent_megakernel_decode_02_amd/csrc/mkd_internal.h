@@ -114,7 +114,8 @@ size_t lds_bytes(const KParams& p);
 // launch the reset kernel and the cooperative megakernel on `stream`
 // ev0/ev1 (may be null) are recorded around the cooperative kernel alone
 int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why);
-// co-resident workgroups of the persistent kernel for `batch` sequences
-int max_coop_blocks(int device, size_t lds, int batch, int* out);
+// co-resident workgroups of the persistent kernel for `batch` sequences of a
+// dense or MoE model
+int max_coop_blocks(int device, size_t lds, int batch, bool moe, int* out);
 
 }  // namespace mkd

@@ -433,11 +433,12 @@ struct Fetch {
 // The first batch of up to three fetches is issued before any is checked, so
 // one round trip covers an instruction's inputs (8192 words of the first,
 // 2048 of the others); longer inputs take further batches.
-// (the first fetch's words land in its destination through m)
-template <int K, class M = InPlace>
+// (the first fetch's words land in its destination through m; S0 16-byte
+// loads per thread per batch of it)
+template <int K, class M = InPlace, int S0 = 8>
 __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count,
                                        M m = M()) {
-  constexpr int S0 = 8, S1 = 2;
+  constexpr int S1 = 2;
   if (!wait_counter(c, stage, step_plus1, count)) return false;
   Staged<S0> st0;
   Staged<S1> st1, st2;
@@ -465,9 +466,9 @@ __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, u
   return true;
 }
 
-template <int K, class M = InPlace>
+template <int K, class M = InPlace, int S0 = 8>
 __device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K], M m = M()) {
-  return gather<K, M>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count, m);
+  return gather<K, M, S0>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count, m);
 }
 
 // RMSNorm gains of this thread's elements (i = tid + k * kThreads), read
@@ -1475,6 +1476,23 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
   const uint32_t tag = tag_of(p, c.t, l);
   const uint16_t* gamma = lptr(p, l, WL_FFN_NORM);
   const Gains gr = load_gains(c, p.d, gamma);
+  // Router logits, one wavefront per expert row.  With d <= 4096 and at most
+  // one expert per wavefront the row is requested with 16-byte loads before
+  // the inputs are waited for (element (k * 64 + lane) * 8 + j of the row in
+  // unit k, lane's j-th value); read element by element after the wait, the
+  // loads were dozens of round trips through a memory system busy with
+  // other workgroups' streams.
+  constexpr int RU = 8;
+  const uint16_t* wr = lptr(p, l, WL_ROUTER);
+  const bool router_early = p.d <= RU * 512 && p.E <= kWaves;
+  u32x4 rw[RU];
+  {
+    const bool mine = router_early && c.wave < p.E;
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc(wr + (size_t)(mine ? c.wave : 0) * p.d, mine ? (uint32_t)p.d * 2u : 0u);
+#pragma unroll
+    for (int k = 0; k < RU; ++k) rw[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (k * 64 + c.lane) * 16, 0, 0);
+  }
   const Fetch f[1] = {{p.hmid, p.d, tag, c.xs}};
   if (!gather_inputs<1>(c, f)) return false;
   rmsnorm_g(c, p.d, gamma, gr);
@@ -1482,13 +1500,31 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
     pad_zero(c, c.xs, p.d);
     __syncthreads();
   }
-  // router logits: one wavefront per expert row
-  const uint16_t* wr = lptr(p, l, WL_ROUTER);
-  for (int e = c.wave; e < p.E; e += kWaves) {
-    float acc = 0.f;
-    for (int i = c.lane; i < p.d; i += 64) acc = fmaf(bf_val(ld_u16(wr + (size_t)e * p.d + i)), c.xs[i], acc);
-    const float z = wave_sum(acc);
-    if (c.lane == 0) c.red[64 + e] = z;
+  if (router_early) {
+    if (c.wave < p.E) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < RU; ++k) {
+        const int i0 = (k * 64 + c.lane) * 8;
+        if (i0 < p.d) {
+          const uint32_t wv[4] = {rw[k].x, rw[k].y, rw[k].z, rw[k].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc = fmaf(bf_lo(wv[j]), c.xs[i0 + 2 * j], acc);
+            acc = fmaf(bf_hi(wv[j]), c.xs[i0 + 2 * j + 1], acc);
+          }
+        }
+      }
+      const float z = wave_sum(acc);
+      if (c.lane == 0) c.red[64 + c.wave] = z;
+    }
+  } else {
+    for (int e = c.wave; e < p.E; e += kWaves) {
+      float acc = 0.f;
+      for (int i = c.lane; i < p.d; i += 64) acc = fmaf(bf_val(ld_u16(wr + (size_t)e * p.d + i)), c.xs[i], acc);
+      const float z = wave_sum(acc);
+      if (c.lane == 0) c.red[64 + e] = z;
+    }
   }
   __syncthreads();
   if (c.tid == 0) {
@@ -1533,13 +1569,20 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
   CKParams& p = c.p;
   const uint32_t tag = tag_of(p, c.t, l);
   const int Fpad = (p.F + 511) & ~511;
-  const Fetch f[4] = {{p.route, 4, tag, c.red + 8}, {p.act, p.F, tag, c.xs},
-                      {p.act + p.F, p.F, tag, c.xs + Fpad}, {p.hmid + a, b - a, tag, c.res}};
   if (p.F & 511) {
+    const Fetch f[4] = {{p.route, 4, tag, c.red + 8}, {p.act, p.F, tag, c.xs},
+                        {p.act + p.F, p.F, tag, c.xs + Fpad}, {p.hmid + a, b - a, tag, c.res}};
     pad_zero(c, c.xs, p.F);
     pad_zero(c, c.xs + Fpad, p.F);
+    if (!gather_inputs<4>(c, f)) return false;
+  } else {
+    // both experts' activations are one contiguous span, in the same layout
+    // in LDS: one fetch, 16 loads per thread per round trip (two round trips
+    // for Mixtral's 2 x 14336 words, against a dozen in 2048-word pieces)
+    const Fetch f[3] = {{p.act, 2 * p.F, tag, c.xs}, {p.hmid + a, b - a, tag, c.res},
+                        {p.route, 4, tag, c.red + 8}};
+    if (!gather_inputs<3, InPlace, 16>(c, f)) return false;
   }
-  if (!gather_inputs<4>(c, f)) return false;
   const int ea = uni(__float_as_int(c.red[8])), eb = uni(__float_as_int(c.red[9]));
   const float wa = __int_as_float(uni(__float_as_int(c.red[10])));
   const float wb = __int_as_float(uni(__float_as_int(c.red[11])));
@@ -1854,12 +1897,16 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
 
 __shared__ int s_flags[8];
 
-// The persistent loop.  Two kernels instantiate it: one sequence (batch
-// size the constant 1, every opcode) and several (batch size from the
-// parameters, dense opcodes only), so that neither carries the other's
-// register pressure.
-template <bool BATCHED>
+// The persistent loop.  Three kernels instantiate it: dense models with one
+// sequence (batch size the constant 1), MoE models with one sequence, and
+// dense models with several sequences (batch size from the parameters).  No
+// kernel carries the others' code: the register allocation and code layout
+// of each stay its own (the batched GEMV in the batch-1 kernel cost it 4%;
+// a change to the MoE opcodes alone moved it by 2%).
+enum KernelKind { K_DENSE = 0, K_MOE = 1, K_BATCH = 2 };
+template <int KIND>
 __device__ __forceinline__ void megakernel_body() {
+  constexpr bool BATCHED = KIND == K_BATCH, MOE = KIND == K_MOE;
   // The parameters are read in place in the kernel-argument segment (they
   // are the first and only argument): referring to the by-value parameter
   // itself would make the compiler copy it to scratch memory.
@@ -1912,10 +1959,10 @@ __device__ __forceinline__ void megakernel_body() {
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
         case OP_MOE_UPGATE:
-          if constexpr (!BATCHED) ok = op_moe_upgate(c, l, a, b, index);
+          if constexpr (MOE) ok = op_moe_upgate(c, l, a, b, index);
           break;
         case OP_MOE_DOWN:
-          if constexpr (!BATCHED) ok = op_moe_down(c, l, a, b);
+          if constexpr (MOE) ok = op_moe_down(c, l, a, b);
           break;
         default: break;
       }
@@ -1942,12 +1989,17 @@ __device__ __forceinline__ void megakernel_body() {
 
 extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams params) {
   (void)params;
-  megakernel_body<false>();
+  megakernel_body<K_DENSE>();
+}
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel_moe(KParams params) {
+  (void)params;
+  megakernel_body<K_MOE>();
 }
 
 extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel_batch(KParams params) {
   (void)params;
-  megakernel_body<true>();
+  megakernel_body<K_BATCH>();
 }
 
 extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
@@ -1966,14 +2018,15 @@ size_t lds_bytes(const KParams& p) {
          (size_t)p.pre_units * kWaves * 1024;
 }
 
-// the persistent kernel for `batch` sequences
-static const void* kernel_for(int batch) {
-  return batch > 1 ? (const void*)mkd_megakernel_batch : (const void*)mkd_megakernel;
+// the persistent kernel for `batch` sequences of a dense or MoE model
+static const void* kernel_for(int batch, bool moe) {
+  return batch > 1 ? (const void*)mkd_megakernel_batch
+                   : (moe ? (const void*)mkd_megakernel_moe : (const void*)mkd_megakernel);
 }
 
-int max_coop_blocks(int device, size_t lds, int batch, int* out) {
+int max_coop_blocks(int device, size_t lds, int batch, bool moe, int* out) {
   if (hipSetDevice(device) != hipSuccess) return MKD_E_HIP;
-  const void* k = kernel_for(batch);
+  const void* k = kernel_for(batch, moe);
   if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return MKD_E_HIP;
   int per_cu = 0, n_cu = 0;
@@ -1993,7 +2046,7 @@ int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(mkd_reset, dim3(blocks), dim3(256), 0, s, p.h, ll_words, p.status);
   if (hipGetLastError() != hipSuccess) { *why = "reset kernel launch failed"; return MKD_E_HIP; }
-  const void* k = kernel_for(p.B);
+  const void* k = kernel_for(p.B, p.E > 0);
   if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     *why = "cannot raise the kernel's LDS limit";
     return MKD_E_HIP;
