@@ -163,6 +163,8 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   if (batch < 1 || batch > kMaxBatch) return fail(MKD_E_INVALID, "batch must be in [1, 8]");
   if (batch > 1 && cfg && cfg->n_experts)
     return fail(MKD_E_UNSUPPORTED, "batched decode is implemented for dense models only");
+  if (batch > 1 && cfg && cfg->d_model > 16 * kThreads)
+    return fail(MKD_E_UNSUPPORTED, "batched decode needs d_model <= 8192");
   size_t want = 0;
   int rc = mkd_weight_count(cfg, &want);
   if (rc) return rc;

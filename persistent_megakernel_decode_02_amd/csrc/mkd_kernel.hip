@@ -1175,17 +1175,48 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
 
 // ---------------------------------------------------------------- several sequences
 
-// sequence b's vector (element i at xs[SlicePad(i * NB + b)]) <- its
-// rmsnorm times gamma[i] (this thread's first gains already in registers)
+// RMSNorm gains of the batched path: this thread's 8-element slices s = tid
+// and s = tid + kThreads (d <= 16 kThreads), 16 bytes each, read before the
+// inputs are waited for.
+struct SliceGains {
+  u32x4 g[2];
+};
+__device__ __forceinline__ SliceGains load_slice_gains(Ctx& c, int d, const uint16_t* gamma) {
+  SliceGains r;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(gamma, (uint32_t)d * 2u);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) r.g[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (c.tid + k * kThreads) * 16, 0, 0);
+  return r;
+}
+
+// Sequence b's vector (element k at xs[SlicePad(k NB + b)]) <- its RMSNorm
+// times gamma.  Each thread takes whole 8-element slices (8 NB floats, read
+// and written as 16-byte vectors; consecutive threads' slices are an odd
+// number of 16-byte units apart, so the accesses spread over all LDS banks).
+// An element-by-element pass over this layout hit a handful of banks and
+// cost 6 us per instruction at NB = 8.  Needs d % 8 == 0 and d <= 16 kThreads.
 template <int NB>
-__device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma, const Gains& gr) {
-  const SlicePad<NB> m;
+__device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const SliceGains& sg) {
+  constexpr int XS = SlicePad<NB>::kStride, V = 2 * NB;   // f32x4 vectors per slice
+  const int nsl = d >> 3;
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
-  for (int i = c.tid; i < d; i += kThreads)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) ss[b] = fmaf(c.xs[m(i * NB + b)], c.xs[m(i * NB + b)], ss[b]);
+  for (int k = 0; k < 2; ++k) {
+    const int sl = c.tid + k * kThreads;
+    if (sl < nsl) {
+      const f32x4* v = (const f32x4*)(c.xs + sl * XS);
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const f32x4 u = v[q];
+        ss[(4 * q + 0) % NB] = fmaf(u.x, u.x, ss[(4 * q + 0) % NB]);
+        ss[(4 * q + 1) % NB] = fmaf(u.y, u.y, ss[(4 * q + 1) % NB]);
+        ss[(4 * q + 2) % NB] = fmaf(u.z, u.z, ss[(4 * q + 2) % NB]);
+        ss[(4 * q + 3) % NB] = fmaf(u.w, u.w, ss[(4 * q + 3) % NB]);
+      }
+    }
+  }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const float w = wave_sum(ss[b]);
@@ -1201,17 +1232,27 @@ __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const uint16_t* gamma, 
     inv[b] = 1.0f / sqrtf(tot / (float)d + c.p.eps);
   }
 #pragma unroll
-  for (int k = 0; k < kGainRegs; ++k) {
-    const int i = c.tid + k * kThreads;
-    if (i < d) {
+  for (int k = 0; k < 2; ++k) {
+    const int sl = c.tid + k * kThreads;
+    if (sl < nsl) {
+      f32x4* v = (f32x4*)(c.xs + sl * XS);
+      const uint32_t gw[4] = {sg.g[k].x, sg.g[k].y, sg.g[k].z, sg.g[k].w};
+      float g[8];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) c.xs[m(i * NB + b)] = (c.xs[m(i * NB + b)] * inv[b]) * gr.g[k];
+      for (int e = 0; e < 4; ++e) {
+        g[2 * e] = bf_lo(gw[e]);
+        g[2 * e + 1] = bf_hi(gw[e]);
+      }
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        f32x4 u = v[q];
+        u.x = (u.x * inv[(4 * q + 0) % NB]) * g[(4 * q + 0) / NB];
+        u.y = (u.y * inv[(4 * q + 1) % NB]) * g[(4 * q + 1) / NB];
+        u.z = (u.z * inv[(4 * q + 2) % NB]) * g[(4 * q + 2) / NB];
+        u.w = (u.w * inv[(4 * q + 3) % NB]) * g[(4 * q + 3) / NB];
+        v[q] = u;
+      }
     }
-  }
-  for (int i = c.tid + kGainRegs * kThreads; i < d; i += kThreads) {
-    const float g = bf_val(ld_u16(gamma + i));
-#pragma unroll
-    for (int b = 0; b < NB; ++b) c.xs[m(i * NB + b)] = (c.xs[m(i * NB + b)] * inv[b]) * g;
   }
   __syncthreads();
 }
@@ -1414,13 +1455,13 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   f[0].n = k1 * NB;
   BatchStream<NB> bs(g, ns, c.wave, c.lane, 0, pseg);
   bs.prefetch();
-  const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
+  const SliceGains sg = load_slice_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
   if (!gemv_inputs(c, a, b, k1, f, embed_x, embed_res, xm)) return false;
   // everything requested so far has arrived (loads complete in order);
   // saying so keeps the waits of the row loop exact
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   bs.prefetch_rest();
-  if (gamma) rmsnorm_b<NB>(c, p.d, gamma, gr);
+  if (gamma) rmsnorm_b<NB>(c, p.d, sg);
   bs.run(c.xs, c.out, false);
   for (int sa = pseg; sa < nseg; sa += pseg) {
     const int sb = min(nseg, sa + pseg);
