@@ -1787,36 +1787,101 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
     for (int i = 0; i < 8; ++i) st.o[g][i] = 0.f;
   }
 
-  for (int s0 = 0; s0 < nsteps; s0 += ARING) {
+  if constexpr (G == 1) {
+    // One q head per instruction (the one-chunk mode of short contexts, a
+    // few steps per wavefront): the running max is updated per position.
+    for (int s0 = 0; s0 < nsteps; s0 += ARING) {
 #pragma unroll
-    for (int d = 0; d < ARING; ++d) {
-      if (s0 + d < nsteps) {
-        const int j = lo + (c.wave + (s0 + d) * kWaves) * PPW + grp;
-        const u32x4 kw = rk[d], vw = rv[d];
-        float kf[8], vf[8];
-        kf[0] = bf_lo(kw.x); kf[1] = bf_hi(kw.x); kf[2] = bf_lo(kw.y); kf[3] = bf_hi(kw.y);
-        kf[4] = bf_lo(kw.z); kf[5] = bf_hi(kw.z); kf[6] = bf_lo(kw.w); kf[7] = bf_hi(kw.w);
-        vf[0] = bf_lo(vw.x); vf[1] = bf_hi(vw.x); vf[2] = bf_lo(vw.y); vf[3] = bf_hi(vw.y);
-        vf[4] = bf_lo(vw.z); vf[5] = bf_hi(vw.z); vf[6] = bf_lo(vw.w); vf[7] = bf_hi(vw.w);
-
-        const bool valid = j < hic;
+      for (int d = 0; d < ARING; ++d) {
+        if (s0 + d < nsteps) {
+          const int j = lo + (c.wave + (s0 + d) * kWaves) * PPW + grp;
+          const u32x4 kw = rk[d], vw = rv[d];
+          float kf[8], vf[8];
+          kf[0] = bf_lo(kw.x); kf[1] = bf_hi(kw.x); kf[2] = bf_lo(kw.y); kf[3] = bf_hi(kw.y);
+          kf[4] = bf_lo(kw.z); kf[5] = bf_hi(kw.z); kf[6] = bf_lo(kw.w); kf[7] = bf_hi(kw.w);
+          vf[0] = bf_lo(vw.x); vf[1] = bf_hi(vw.x); vf[2] = bf_lo(vw.y); vf[3] = bf_hi(vw.y);
+          vf[4] = bf_lo(vw.z); vf[5] = bf_hi(vw.z); vf[6] = bf_lo(vw.w); vf[7] = bf_hi(vw.w);
+          const bool valid = j < hic;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float s = 0.f;
+          for (int g = 0; g < G; ++g) {
+            float sv = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s = fmaf(q[g][i], kf[i], s);
-          s = (LPR == 8) ? sum8(s) : sum16(s);
-          if (valid) {
-            const float M = fmaxf(st.m[g], s);
-            const float a = exp2f(st.m[g] - M), e = exp2f(s - M);
-            st.l[g] = st.l[g] * a + e;
+            for (int i = 0; i < 8; ++i) sv = fmaf(q[g][i], kf[i], sv);
+            sv = (LPR == 8) ? sum8(sv) : sum16(sv);
+            if (valid) {
+              const float M = fmaxf(st.m[g], sv);
+              const float a = exp2f(st.m[g] - M), e = exp2f(sv - M);
+              st.l[g] = st.l[g] * a + e;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) st.o[g][i] = fmaf(st.o[g][i], a, e * vf[i]);
-            st.m[g] = M;
+              for (int i = 0; i < 8; ++i) st.o[g][i] = fmaf(st.o[g][i], a, e * vf[i]);
+              st.m[g] = M;
+            }
           }
         }
+        issue(rk[d], rv[d]);
       }
-      issue(rk[d], rv[d]);
+    }
+  } else {
+    // Online softmax one block of ARING positions at a time (per lane group):
+    // the block's scores first, then one running-max update and one rescale
+    // of (l, o) per head, then e = 2^(s - m) and o += e v per position.  Per
+    // position that is one exponential and 8 FMAs on o, against two
+    // exponentials and a rescale of o when the running max moves per position;
+    // at long context attention is bound by this arithmetic.
+    for (int s0 = 0; s0 < nsteps; s0 += ARING) {
+      float sc[ARING][G];
+  #pragma unroll
+      for (int d = 0; d < ARING; ++d) {
+  #pragma unroll
+        for (int g = 0; g < G; ++g) sc[d][g] = -INFINITY;
+        if (s0 + d >= nsteps) continue;   // past this wavefront's last step (uniform)
+        const int j = lo + (c.wave + (s0 + d) * kWaves) * PPW + grp;
+        const bool valid = j < hic;
+        const u32x4 kw = rk[d];
+        float kf[8];
+        kf[0] = bf_lo(kw.x); kf[1] = bf_hi(kw.x); kf[2] = bf_lo(kw.y); kf[3] = bf_hi(kw.y);
+        kf[4] = bf_lo(kw.z); kf[5] = bf_hi(kw.z); kf[6] = bf_lo(kw.w); kf[7] = bf_hi(kw.w);
+  #pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float sv = 0.f;
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) sv = fmaf(q[g][i], kf[i], sv);
+          sv = (LPR == 8) ? sum8(sv) : sum16(sv);
+          sc[d][g] = valid ? sv : -INFINITY;
+        }
+      }
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float M = st.m[g];
+  #pragma unroll
+        for (int d = 0; d < ARING; ++d) M = fmaxf(M, sc[d][g]);
+        if (M != -INFINITY) {
+          const float a = exp2f(st.m[g] - M);   // 0 while nothing was seen
+          st.l[g] *= a;
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) st.o[g][i] *= a;
+          st.m[g] = M;
+        }
+      }
+  #pragma unroll
+      for (int d = 0; d < ARING; ++d) {
+        if (s0 + d < nsteps) {   // uniform
+          const u32x4 vw = rv[d];
+          float vf[8];
+          vf[0] = bf_lo(vw.x); vf[1] = bf_hi(vw.x); vf[2] = bf_lo(vw.y); vf[3] = bf_hi(vw.y);
+          vf[4] = bf_lo(vw.z); vf[5] = bf_hi(vw.z); vf[6] = bf_lo(vw.w); vf[7] = bf_hi(vw.w);
+  #pragma unroll
+          for (int g = 0; g < G; ++g) {
+            // an invalid position has score -inf: e = 0 (m is finite once any
+            // position of the block was valid; otherwise the block adds nothing)
+            const float e = sc[d][g] == -INFINITY ? 0.f : exp2f(sc[d][g] - st.m[g]);
+            st.l[g] += e;
+  #pragma unroll
+            for (int i = 0; i < 8; ++i) st.o[g][i] = fmaf(e, vf[i], st.o[g][i]);
+          }
+        }
+        issue(rk[d], rv[d]);
+      }
     }
   }
 
