@@ -1677,6 +1677,9 @@ __device__ __forceinline__ void merge_into(AttnState<G>& s, const float* om, con
 template <int HD, int G>
 __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int q0, bool may_append) {
   CKParams& p = c.p;
+  // K/V position steps in flight per lane: 6 for the grouped split-KV
+  // instructions (measured best of 4, 6, 8 at KV 4096-32768)
+  constexpr int AR = G > 1 ? 6 : ARING;
   constexpr int LPR = HD / 8;     // lanes per K/V row
   constexpr int PPW = 64 / LPR;   // positions per wavefront load
   const int seq = c.seq;
@@ -1700,7 +1703,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   // positions lo + j*PPW + [0, PPW), lane group grp takes one of them
   const int nblk = hic > lo ? (hic - lo + PPW - 1) / PPW : 0;
   const int nsteps = nblk > c.wave ? (nblk - c.wave + kWaves - 1) / kWaves : 0;
-  u32x4 rk[ARING], rv[ARING];
+  u32x4 rk[AR], rv[AR];
   int pstep = 0;
   // positions past the chunk use an offset beyond the buffer range: the load
   // returns zeros without touching memory, so every issue is unconditional
@@ -1712,7 +1715,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
     ++pstep;
   };
 #pragma unroll
-  for (int d = 0; d < ARING; ++d) issue(rk[d], rv[d]);
+  for (int d = 0; d < AR; ++d) issue(rk[d], rv[d]);
 
   // inputs: raw q of the G heads, k and v of this kv head
   float* qs = c.xs;                 // [G][HD]
@@ -1790,9 +1793,9 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   if constexpr (G == 1) {
     // One q head per instruction (the one-chunk mode of short contexts, a
     // few steps per wavefront): the running max is updated per position.
-    for (int s0 = 0; s0 < nsteps; s0 += ARING) {
+    for (int s0 = 0; s0 < nsteps; s0 += AR) {
 #pragma unroll
-      for (int d = 0; d < ARING; ++d) {
+      for (int d = 0; d < AR; ++d) {
         if (s0 + d < nsteps) {
           const int j = lo + (c.wave + (s0 + d) * kWaves) * PPW + grp;
           const u32x4 kw = rk[d], vw = rv[d];
@@ -1822,16 +1825,16 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
       }
     }
   } else {
-    // Online softmax one block of ARING positions at a time (per lane group):
+    // Online softmax one block of AR positions at a time (per lane group):
     // the block's scores first, then one running-max update and one rescale
     // of (l, o) per head, then e = 2^(s - m) and o += e v per position.  Per
     // position that is one exponential and 8 FMAs on o, against two
     // exponentials and a rescale of o when the running max moves per position;
     // at long context attention is bound by this arithmetic.
-    for (int s0 = 0; s0 < nsteps; s0 += ARING) {
-      float sc[ARING][G];
+    for (int s0 = 0; s0 < nsteps; s0 += AR) {
+      float sc[AR][G];
   #pragma unroll
-      for (int d = 0; d < ARING; ++d) {
+      for (int d = 0; d < AR; ++d) {
   #pragma unroll
         for (int g = 0; g < G; ++g) sc[d][g] = -INFINITY;
         if (s0 + d >= nsteps) continue;   // past this wavefront's last step (uniform)
@@ -1854,7 +1857,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
       for (int g = 0; g < G; ++g) {
         float M = st.m[g];
   #pragma unroll
-        for (int d = 0; d < ARING; ++d) M = fmaxf(M, sc[d][g]);
+        for (int d = 0; d < AR; ++d) M = fmaxf(M, sc[d][g]);
         if (M != -INFINITY) {
           const float a = exp2f(st.m[g] - M);   // 0 while nothing was seen
           st.l[g] *= a;
@@ -1864,7 +1867,7 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
         }
       }
   #pragma unroll
-      for (int d = 0; d < ARING; ++d) {
+      for (int d = 0; d < AR; ++d) {
         if (s0 + d < nsteps) {   // uniform
           const u32x4 vw = rv[d];
           float vf[8];
