@@ -327,7 +327,7 @@ static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch, 
   x = x > act ? x : act;
   const int lm = 2 * n_lm * batch;                      // every sequence's LM-head partials
   x = x > lm ? x : lm;
-  const int ared = n_chunks * (hd + 2);
+  const int ared = n_chunks * (hd + 2) + 4 * hd;   // a head's chunk partials, then quarter sums
   x = x > ared ? x : ared;
   const int attn = (G + 2) * hd + kWaves * G * (hd + 2);
   x = x > attn ? x : attn;

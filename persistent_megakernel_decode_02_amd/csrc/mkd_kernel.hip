@@ -1981,23 +1981,39 @@ __device__ __forceinline__ bool op_attn_hd(Ctx& c, int l, int a, int b) {
 
 // ---------------------------------------------------------------- opcode: split-KV reduction
 
+// Wavefront 0 turns the chunks' maxima into their weights 2^(m_k - M) (one
+// lane per chunk, n <= 64) and the normaliser sum_k l_k 2^(m_k - M); then
+// the workgroup's threads split (element, chunk quarter) and add up the
+// weighted partial outputs, the quarters in a fixed order.
 __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
   CKParams& p = c.p;
   const int HD = p.hd, n = p.n_chunks, W = HD + 2;
   const uint32_t tag = tag_of(p, c.t, l);
   const Fetch f[1] = {{p.part + (size_t)c.seq * p.s_part + (size_t)qh * n * W, n * W, tag, c.xs}};
   if (!gather_inputs<1>(c, f)) return false;
-  for (int i = c.tid; i < HD; i += kThreads) {
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, c.xs[k * W]);
-    float L = 0.f, O = 0.f;
-    for (int k = 0; k < n; ++k) {
-      const float a = exp2f(c.xs[k * W] - M);
-      L = fmaf(c.xs[k * W + 1], a, L);
-      O = fmaf(c.xs[k * W + 2 + i], a, O);
-    }
-    ll_store(p.aout + (size_t)(qh * HD + i) * c.B + c.seq, O / L, tag);
+  float* const wk = c.red + 128;   // [64] chunk weights, then [4][HD <= 128] quarter sums below
+  if (c.wave == 0) {
+    const float m = c.lane < n ? c.xs[c.lane * W] : -INFINITY;
+    float M = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float a = c.lane < n ? exp2f(m - M) : 0.f;
+    const float L = wave_sum(c.lane < n ? c.xs[c.lane * W + 1] * a : 0.f);
+    wk[c.lane] = a / L;   // weight of chunk `lane`, normalised
   }
+  __syncthreads();
+  // thread (quarter q, element i): chunks q, q + 4, ...
+  float* const qs = c.xs + n * W;   // [4][HD] quarter sums, after the partials
+  if (c.tid < 4 * HD) {
+    const int q = c.tid / HD, i = c.tid - q * HD;
+    float O = 0.f;
+    for (int k = q; k < n; k += 4) O = fmaf(c.xs[k * W + 2 + i], wk[k], O);
+    qs[q * HD + i] = O;
+  }
+  __syncthreads();
+  for (int i = c.tid; i < HD; i += kThreads)
+    ll_store(p.aout + (size_t)(qh * HD + i) * c.B + c.seq,
+             (qs[i] + qs[HD + i]) + (qs[2 * HD + i] + qs[3 * HD + i]), tag);
   __syncthreads();
   return true;
 }
