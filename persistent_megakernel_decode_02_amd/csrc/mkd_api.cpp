@@ -57,7 +57,7 @@ struct mkd_model {
   size_t sched_words = 0, sched_cap = 0;
   int batch = 1;  // sequences decoded together
   int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, res_floats = 0;
-  int pre_units = 0, n_stages = 0;
+  int pre_units = 0, pre_off = 0, n_stages = 0;
   int32_t s_qkv = 0, s_part = 0;  // per-sequence strides of qkv and part (words)
   int flag_stride = 0;
   hipEvent_t done = nullptr;
@@ -311,16 +311,21 @@ static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max) {
 
 static int32_t round16i(int64_t n) { return (int32_t)((n + 15) / 16 * 16); }
 
+// LDS floats of one input vector of n elements per sequence: one sequence
+// reads x in 512-wide segments; with several sequences, interleaved, every
+// 8-element slice (8 * batch floats) is followed by 4 padding floats
+static int vec_floats(int n, int batch) {
+  const int padded = (n + 511) & ~511;
+  return batch == 1 ? padded : padded / 8 * (8 * batch + 4);
+}
+
 // LDS floats for the staged input vectors (and the other staging uses of
 // that area); with_act false leaves out the down projection's input, which
 // several sequences may stream in passes over K (one segment at least)
 static int x_floats_for(const mkd_config* c, int n_chunks, int n_lm, int batch, bool with_act = true) {
   const int G = c->n_q_heads / c->n_kv_heads, hd = c->head_dim;
   const int qd = c->n_q_heads * hd;
-  auto pad = [](int n) { return (n + 511) & ~511; };   // streamer rows read x in 512-wide segments
-  // one input vector per sequence, interleaved; with several sequences every
-  // 8-element slice (8 * batch floats) is followed by 4 padding floats
-  auto vec = [&](int n) { return batch == 1 ? pad(n) : pad(n) / 8 * (8 * batch + 4); };
+  auto vec = [&](int n) { return vec_floats(n, batch); };
   int x = vec(c->d_model);
   x = x > vec(qd) ? x : vec(qd);
   const int act = with_act ? vec(c->d_ff) * (c->top_k ? c->top_k : 1) : vec(512);
@@ -348,15 +353,54 @@ static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int b
   if (const char* e = getenv("MKD_BATCH_X_FLOATS")) {
     const int seg = 64 * (8 * batch + 4);   // one 512-element segment of every sequence, padded
     const int cap = atoi(e) / seg * seg;
-    if (cap > 0 && cap < p.x_floats && cap >= x_floats_for(c, n_chunks, n_lm, batch, false)) p.x_floats = cap;
+    if (cap > 0 && cap < p.x_floats && cap >= x_floats_for(c, n_chunks, n_lm, batch, false)) {
+      p.x_floats = cap;
+      return;
+    }
   }
-  if (lds_max <= 0 || lds_bytes(p) + kLdsSlack <= (size_t)lds_max) return;
+  if (lds_max <= 0) return;
   const size_t other = lds_bytes(p) - (size_t)p.x_floats * sizeof(float);
   if (other + kLdsSlack >= (size_t)lds_max) return;
-  int x = (int)(((size_t)lds_max - kLdsSlack - other) / sizeof(float));
+  const int fill = (int)(((size_t)lds_max - kLdsSlack - other) / sizeof(float)) & ~3;
+  if (fill >= p.x_floats) {
+    // it fits: the area grows to the whole LDS left, and the part past the
+    // gate/up and O-projection inputs holds staged gate/up weights
+    p.x_floats = fill;
+    return;
+  }
   const int seg = 64 * (8 * batch + 4);
-  x = x / seg * seg;
+  const int x = fill / seg * seg;
   if (x >= x_floats_for(c, n_chunks, n_lm, batch, false)) p.x_floats = x;
+}
+
+// Gate/up weight units staged in LDS ahead of their instruction.  One
+// sequence: the LDS left after everything else (pre_units_for).  Several:
+// the input area past the two inputs that are live while the units are
+// (the O-projection's, read while they load, and gate/up's own); the down
+// projection's longer input reuses that space after gate/up has read them.
+static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max) {
+  p.pre_off = 0;
+  if (batch == 1) {
+    p.pre_units = pre_units_for(c, lds_bytes(p), lds_max);
+    return;
+  }
+  p.pre_units = 0;
+  if (c->n_experts > 0) return;
+  // measured: with the down projection in passes over K (larger batches)
+  // staging slows the step down
+  if (p.x_floats < vec_floats(c->d_ff, batch)) return;
+  const int qd = c->n_q_heads * c->head_dim;
+  const int off = (std::max(vec_floats(c->d_model, batch), vec_floats(qd, batch)) + 3) & ~3;
+  if (off >= p.x_floats) return;
+  int n = (p.x_floats - off) / (kWaves * 256);   // 1 KiB units per wavefront
+  n = std::min(n, kPreMax);
+  if (const char* e = getenv("MKD_PRE_UNITS")) {
+    const int want = atoi(e);
+    if (want >= 0 && want < n) n = want;
+  }
+  if (n < 4) return;   // the batched streamer stages whole groups of 4 rows
+  p.pre_off = off;
+  p.pre_units = n;
 }
 
 int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
@@ -372,7 +416,7 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
     int lds_max = 0;
     hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
     fit_x(p, &m->cfg, 1, n_lm, m->batch, lds_max);
-    p.pre_units = m->batch == 1 ? pre_units_for(&m->cfg, lds_bytes(p), lds_max) : 0;
+    set_pre(p, &m->cfg, m->batch, lds_max);
     int mx = 0;
     const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, m->cfg.n_experts > 0, &mx);
     if (rc) return fail(rc, "occupancy query failed");
@@ -401,7 +445,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
   fit_x(p, c, n_chunks, n_lm, batch, lds_max);
-  p.pre_units = batch == 1 ? pre_units_for(c, lds_bytes(p), lds_max) : 0;
+  set_pre(p, c, batch, lds_max);
   const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
@@ -473,6 +517,7 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   m->out_floats = out_floats;
   m->res_floats = res_floats;
   m->pre_units = p.pre_units;
+  m->pre_off = p.pre_off;
   m->s_qkv = s_qkv; m->s_part = s_part;
   return MKD_OK;
 }
@@ -564,6 +609,7 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   p.out_floats = m->out_floats;
   p.res_floats = m->res_floats;
   p.pre_units = m->pre_units;
+  p.pre_off = m->pre_off;
   p.eps = c->rms_eps;
   const char* why = "";
   const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, &why);

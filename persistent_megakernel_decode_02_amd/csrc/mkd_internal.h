@@ -107,6 +107,9 @@ struct KParams {
   int32_t res_floats;        // LDS floats for the residual rows of a tile (all sequences)
   int32_t pre_units;         // dense gate/up: 1 KiB weight units per wavefront staged in LDS
                              // by the instruction before it (0 = none)
+  int32_t pre_off;           // where those units sit: 0 = their own area after the reduction
+                             // scratch; else this many floats into the input area, past the
+                             // gate/up and O-projection inputs (several sequences)
   float eps;
 };
 

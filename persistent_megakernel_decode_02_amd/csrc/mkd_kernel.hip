@@ -1,4 +1,6 @@
-// Persistent batch-1 decode megakernel for gfx950 (MI355X).
+// Persistent decode megakernel for gfx950 (MI355X): one sequence (dense or
+// MoE model) or 2-8 sequences decoded together (dense), each its own
+// instantiation of the same persistent loop.
 //
 // One cooperative launch; one 512-thread workgroup per compute unit; every
 // workgroup walks its slice of a host-built instruction tensor for every
@@ -317,7 +319,6 @@ __device__ __forceinline__ void ll_fetch_from(Ctx& c, const uint64_t* src, int n
     ll_finish<S, M>(c, sp, base, st, n, tag, dst, m);
   }
 }
-
 template <class M = InPlace>
 __device__ __forceinline__ void ll_fetch(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst, M m = M()) {
   ll_fetch_from<8, M>(c, src, n, tag, dst, 0, m);
@@ -1274,24 +1275,14 @@ __device__ __forceinline__ void rmsnorm_b(Ctx& c, int d, const SliceGains& sg) {
 // (all of them measured best: deeper rings and later refills were slower).
 // Loads past the wavefront's last row use zero-size descriptors, so every
 // refill is issued without a branch.
-template <int NB>
-struct BatchStream {
-  static constexpr int G = 4, D = 3, DPRE = 3;
-  const GemvDesc& g;
-  const int K, nseg, ns;
+// How a batched GEMV instruction's ns rows of nseg 512-element segments are
+// split over the wavefronts: a WR x WS grid, wavefront (wr, ws) takes rows
+// wr, wr + WR, ... and segments ws, ws + WS, ... of [s0, s1); it streams
+// them in steps of kBatchRows rows by one segment, row groups outermost.
+constexpr int kBatchRows = 4;
+struct BatchGrid {
   int WR, WS, wr, ws, nrow, nsw, steps;
-  const uint32_t lane16;
-  int pg, pi;                       // producer: row group, segment (of this wavefront's)
-  __amdgpu_buffer_rsrc_t pr[G];     // the producer group's row descriptors
-  u32x4 ring[D][G];
-
-  // Segments [s0, s1) of every row (one pass; the input slice of segment s
-  // is at xs + (s - s0) * 512 NB).  The wavefront grid depends on the whole
-  // row length, so every pass of an instruction splits the work alike.
-  const int s0;
-  __device__ __forceinline__ BatchStream(const GemvDesc& g_, int ns_, int wave, int lane, int s0_, int s1_)
-      : g(g_), K(uni(g_.K)), nseg(uni((g_.K + 511) >> 9)), ns(uni(ns_)), lane16((uint32_t)lane * 16u),
-        pg(0), pi(0), s0(uni(s0_)) {
+  __device__ __forceinline__ BatchGrid(int ns, int nseg, int wave, int s0, int s1) {
     WR = kWaves;
     WS = 1;
     while (WR > 1 && ns < 4 * WR && 2 * WS <= nseg) {
@@ -1301,9 +1292,46 @@ struct BatchStream {
     wr = wave / WS;
     ws = wave % WS;
     nrow = ns > wr ? (ns - wr + WR - 1) / WR : 0;
-    const int span = uni(s1_) - s0;
+    const int span = s1 - s0;
     nsw = span > ws ? (span - ws + WS - 1) / WS : 0;
-    steps = ((nrow + G - 1) / G) * nsw;
+    steps = ((nrow + kBatchRows - 1) / kBatchRows) * nsw;
+  }
+};
+
+// This wavefront's gate/up units staged in LDS (several sequences): they sit
+// in the input area, past the inputs of gate/up and of the O-projection
+__device__ __forceinline__ u32x4* pre_area_b(Ctx& c) {
+  return (u32x4*)(c.xs + c.p.pre_off) + (size_t)c.wave * c.p.pre_units * 64;
+}
+
+template <int NB>
+struct BatchStream {
+  static constexpr int G = kBatchRows, D = 3, DPRE = 3;
+  const GemvDesc& g;
+  const int K, nseg, ns;
+  int WR, WS, wr, ws, nrow, nsw, steps;
+  const int U;                      // leading steps already staged in LDS (gate/up)
+  const uint32_t lane16;
+  int pg, pi;                       // producer: row group, segment (of this wavefront's)
+  __amdgpu_buffer_rsrc_t pr[G];     // the producer group's row descriptors
+  u32x4 ring[D][G];
+
+  // Segments [s0, s1) of every row (one pass; the input slice of segment s
+  // is at xs + (s - s0) * 512 NB).  The wavefront grid depends on the whole
+  // row length, so every pass of an instruction splits the work alike.  The
+  // first U steps of this wavefront were loaded into LDS beforehand, in
+  // step order (stage_upgate_b); the stream starts after them.
+  const int s0;
+  __device__ __forceinline__ BatchStream(const GemvDesc& g_, int ns_, int wave, int lane, int s0_, int s1_,
+                                         int staged = 0)
+      : g(g_), K(uni(g_.K)), nseg(uni((g_.K + 511) >> 9)), ns(uni(ns_)), U(uni(staged)),
+        lane16((uint32_t)lane * 16u), pg(0), pi(0), s0(uni(s0_)) {
+    const BatchGrid q(ns, nseg, wave, s0, uni(s1_));
+    WR = q.WR; WS = q.WS; wr = q.wr; ws = q.ws; nrow = q.nrow; nsw = q.nsw; steps = q.steps;
+    if (U > 0) {
+      pg = U / nsw;
+      pi = U - pg * nsw;
+    }
     set_group();
   }
   // stream row k of the tile: output row a + k (or a + k/2, gate or up)
@@ -1342,7 +1370,7 @@ struct BatchStream {
   // Row results: out[k * NB + b] when WS == 1, else this wavefront's partial
   // at out[(ns + ws * ns + k) * NB + b] (combine() adds them up); a pass after
   // the first adds to what the earlier passes left there.
-  __device__ __forceinline__ void run(const float* xs, float* out, bool add) {
+  __device__ __forceinline__ void run(const float* xs, float* out, bool add, const u32x4* pre = nullptr) {
     constexpr int XS = SlicePad<NB>::kStride;
     const float* xl = xs + lane16 / 16u * XS;   // this lane's slice of segment s0
     float acc[G][NB];
@@ -1401,8 +1429,15 @@ struct BatchStream {
         ++cg;
       }
     };
-    for (int s0 = 0; s0 < steps; s0 += D) {
-      if (s0 + D < steps) {
+    for (int s = 0; s < U; ++s) {
+      u32x4 w[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) w[r] = pre[(s * G + r) * 64 + (lane16 >> 4)];
+      eat(w);
+    }
+    const int rs = steps - U;
+    for (int s0 = 0; s0 < rs; s0 += D) {
+      if (s0 + D < rs) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           eat(ring[d]);
@@ -1411,7 +1446,7 @@ struct BatchStream {
       } else {
 #pragma unroll
         for (int d = 0; d < D; ++d)
-          if (s0 + d < steps) eat(ring[d]);
+          if (s0 + d < rs) eat(ring[d]);
       }
     }
   }
@@ -1453,7 +1488,11 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   }
   const int k1 = min(g.K, pseg * 512);
   f[0].n = k1 * NB;
-  BatchStream<NB> bs(g, ns, c.wave, c.lane, 0, pseg);
+  // gate/up steps the previous instruction staged in LDS (stage_upgate_b)
+  const int staged = op == OP_UPGATE && c.instr > 0 && pseg == nseg
+                         ? min(BatchGrid(ns, nseg, c.wave, 0, nseg).steps, p.pre_units / kBatchRows)
+                         : 0;
+  BatchStream<NB> bs(g, ns, c.wave, c.lane, 0, pseg, staged);
   bs.prefetch();
   const SliceGains sg = load_slice_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
   if (!gemv_inputs(c, a, b, k1, f, embed_x, embed_res, xm)) return false;
@@ -1462,7 +1501,7 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   bs.prefetch_rest();
   if (gamma) rmsnorm_b<NB>(c, p.d, sg);
-  bs.run(c.xs, c.out, false);
+  bs.run(c.xs, c.out, false, pre_area_b(c));
   for (int sa = pseg; sa < nseg; sa += pseg) {
     const int sb = min(nseg, sa + pseg);
     const int ka = sa * 512, kb = min(g.K, sb * 512);
@@ -1481,6 +1520,40 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
   bs.combine(c, c.out);
   gemv_epilogue<NB>(c, op, l, a, b, index, tag);
   return true;
+}
+
+// Several sequences: load the first steps of this wavefront's share of a
+// gate/up instruction [a, b) of layer l into LDS, in the order the batched
+// streamer consumes them (BatchGrid), as many whole steps of kBatchRows
+// 1 KiB units as pre_units holds.  Same timing as stage_upgate.
+__device__ __forceinline__ void stage_upgate_b(Ctx& c, int l, int a, int b) {
+  CKParams& p = c.p;
+  GemvDesc g;
+  desc_init(g, a, c.wave);
+  desc_upgate(p, l, g);
+  const int nseg = (g.K + 511) >> 9;
+  const BatchGrid q(2 * (b - a), nseg, c.wave, 0, nseg);
+  const int n = min(q.steps, p.pre_units / kBatchRows);
+  __attribute__((address_space(3))) char* dst = (__attribute__((address_space(3))) char*)pre_area_b(c);
+  int pg = 0, pi = 0;
+  for (int j = 0; j < n; ++j) {
+    const int seg = q.ws + pi * q.WS;
+#pragma unroll
+    for (int r = 0; r < kBatchRows; ++r) {
+      const int i = pg * kBatchRows + r;
+      if (i < q.nrow) {
+        const int k = q.wr + i * q.WR;   // row k of the tile: gate or up row a + k/2
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(row_of(g, a + (k >> 1), k & 1), (uint32_t)g.K * 2u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + (j * kBatchRows + r) * 1024, 16, c.lane * 16,
+                                                 seg * 1024, 0, kNT);
+      }
+    }
+    if (++pi == q.nsw) {
+      pi = 0;
+      ++pg;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // dense GEMV opcodes: several sequences (batched kernel) by their count;
@@ -2074,7 +2147,10 @@ __device__ __forceinline__ void megakernel_body() {
       // loads are done.
       const int32_t* nx = i + 1 < n ? ins + kWords : nullptr;
       const bool stage = p.pre_units > 0 && nx && ldc_i32(nx + I_OP) == OP_UPGATE;
-      if (stage && op == OP_OPROJ) stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+      if (stage && op == OP_OPROJ) {
+        if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+        else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+      }
       switch (op) {
         case OP_QKV:
         case OP_OPROJ:
@@ -2092,7 +2168,10 @@ __device__ __forceinline__ void megakernel_body() {
         default: break;
       }
       if (ok) signal_done(c);
-      if (ok && stage && op != OP_OPROJ) stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+      if (ok && stage && op != OP_OPROJ) {
+        if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+        else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+      }
     }
   }
   // the last step's argmax
@@ -2140,7 +2219,7 @@ extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
 
 size_t lds_bytes(const KParams& p) {
   return ((size_t)p.x_floats + (size_t)p.res_floats + (size_t)p.out_floats + kRed) * sizeof(float) +
-         (size_t)p.pre_units * kWaves * 1024;
+         (p.pre_off ? 0 : (size_t)p.pre_units * kWaves * 1024);
 }
 
 // the persistent kernel for `batch` sequences of a dense or MoE model

@@ -76,6 +76,23 @@ def test_tiny_batched_down_projection_in_passes(B, n_wg, n_chunks, monkeypatch):
     _check_against_oracle(cfg, starts, N, res, 0.1)
 
 
+@pytest.mark.parametrize("B,n_wg", [(2, 7), (4, 256), (3, 33)])
+def test_tiny_batched_staged_gate_up_bit_exact(B, n_wg, monkeypatch):
+    """Gate/up weight rows staged in LDS during the attention phase are consumed in
+    the order the streamer would load them, so the results are bit-identical to a
+    launch with no staging (MKD_PRE_UNITS=0). n_wg 7 stages 4 of a wavefront's 7
+    steps (the rest streamed); n_wg 256 stages every step."""
+    require_gpu()
+    cfg = synth.PRESETS["tiny"]
+    starts, N = STARTS[:B], 4
+    staged = _run_batched(cfg, starts, N, n_wg, 1, 0.1)
+    monkeypatch.setenv("MKD_PRE_UNITS", "0")
+    plain = _run_batched(cfg, starts, N, n_wg, 1, 0.1)
+    assert np.array_equal(staged[0], plain[0]), "tokens differ with staging"
+    assert np.array_equal(staged[1], plain[1]), "logits differ with staging"
+    assert np.array_equal(staged[2], plain[2]), "caches differ with staging"
+
+
 def test_llama1b_batched_full_size_b8():
     """Eight sequences on the 1B shape: the interleaved down-projection input
     (8192 x 8 floats) does not fit in LDS, so it streams in passes over K."""
