@@ -42,7 +42,8 @@ struct StageDesc {
 int config_check(const mkd_config* c, const char** why);
 void stage_list(const mkd_config* c, int n_chunks, int batch, StageDesc* out, int* n_out, int cap);
 int stage_count(const mkd_config* c, int n_chunks);
-// blocks stage s may use, and the first of them (spec v3 placement)
+// blocks stage s may use, and the first of them (the OPROJ stage skips the
+// workgroups of the attention stage before it)
 void placement(const std::vector<StageDesc>& st, int s, int n_wg, int* avail, int* first);
 bool is_tiled(int op);  // stages whose instructions are row tiles
 int schedule_build(const mkd_config* c, int n_wg, int n_chunks, int batch, int32_t* out, size_t cap,
