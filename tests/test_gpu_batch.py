@@ -103,11 +103,13 @@ def test_llama1b_batched_full_size_b8():
     _check_against_oracle(cfg, starts, N, res, 0.0)
 
 
-def test_llama1b_batched_full_size():
-    """Four sequences at different cache lengths around 128 on the 1B shape."""
+@pytest.mark.parametrize("starts", [[128, 96, 131, 64], [128, 300]])
+def test_llama1b_batched_full_size(starts):
+    """Four and two sequences at different cache lengths on the 1B shape (gate/up
+    rows staged in LDS: 3 of each wavefront's 8 steps at B = 4, 4 at B = 2)."""
     require_gpu()
     cfg = synth.PRESETS["llama1b"]
-    starts, N = [128, 96, 131, 64], 3
+    N = 3
     res = _run_batched(cfg, starts, N, 0, 0, 0.0)
     _check_against_oracle(cfg, starts, N, res, 0.0)
 
