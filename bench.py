@@ -103,8 +103,8 @@ def main() -> int:
                     help="sequences decoded together (all from the same KV length)")
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--n-chunks", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=384,
-                    help="oracle decode steps timed on the host, about 10 s (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=640,
+                    help="oracle decode steps timed on the host, 10-30 s (0 = skip)")
     ap.add_argument("--trace", action="store_true", help="per-opcode time breakdown (stderr)")
     ap.add_argument("--calib-copy", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
