@@ -161,6 +161,20 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
  * launch of the megakernel can hold on it. */
 int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg);
 
+/* Host-only query (no device needed): the LDS areas, in floats, that a
+ * schedule of n_wg workgroups and n_chunks split-KV chunks for `batch`
+ * sequences uses per workgroup on a device with lds_max bytes of LDS per
+ * workgroup (0 = unknown: no fitting).  out[6] (caller-owned) receives
+ * {input area, row results, residual rows, staged weight units per
+ * wavefront (1 KiB each), offset of those units inside the input area
+ * (0 = an area of their own after the others), total bytes}.  The staged
+ * units are the next instruction's weights loaded ahead of it (epic-kernel
+ * README, "L2 prefetching overlapped with prior instructions"): dense
+ * gate/up rows, loaded while the workgroup waits out the attention phase.
+ * MKD_E_INVALID for a bad config or argument. */
+int mkd_lds_plan(const mkd_config* cfg, int32_t batch, int32_t n_wg, int32_t n_chunks, int32_t lds_max,
+                 int32_t* out);
+
 /* Build (as mkd_schedule_build) and upload the schedule the next launches
  * use; n_wg = 0 means one workgroup per compute unit; n_chunks = 0 picks a
  * split so that each chunk covers about 32 KiB of K and V at the handle's

@@ -35,7 +35,7 @@ OPCODE_NAMES = {1: "QKV", 2: "ATTN", 3: "AREDUCE", 4: "OPROJ", 5: "UPGATE", 6: "
 EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_count",
            "mkd_weight_shape", "mkd_kv_cache_bytes", "mkd_schedule_build",
            "mkd_schedule_build_batch", "mkd_schedule_validate", "mkd_init", "mkd_init_batch",
-           "mkd_device_info", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
+           "mkd_device_info", "mkd_lds_plan", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
            "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
            "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_destroy")
 
@@ -90,6 +90,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_init": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
         "mkd_init_batch": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
         "mkd_device_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
+        "mkd_lds_plan": ([cfgp, I32, I32, I32, I32, ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_build_schedule": ([P, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_load_schedule": ([P, P, SZ], ctypes.c_int),
         "mkd_decode": ([P, I32, I32, I32, P, P, P, P], ctypes.c_int),
@@ -207,6 +208,13 @@ def mkd_device_info(m: int):
     n_cu, mx = ctypes.c_int32(), ctypes.c_int32()
     _check(load().mkd_device_info(m, ctypes.byref(n_cu), ctypes.byref(mx)))
     return n_cu.value, mx.value
+
+
+def mkd_lds_plan(cfg: mkd_config, batch: int, n_wg: int, n_chunks: int, lds_max: int) -> dict:
+    out = (ctypes.c_int32 * 6)()
+    _check(load().mkd_lds_plan(ctypes.byref(cfg), batch, n_wg, n_chunks, lds_max, out))
+    keys = ("x_floats", "out_floats", "res_floats", "pre_units", "pre_off", "lds_bytes")
+    return dict(zip(keys, list(out)))
 
 
 def mkd_build_schedule(m: int, n_wg: int = 0, n_chunks: int = 0, want_words: bool = False):

@@ -403,20 +403,45 @@ static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max) {
   p.pre_units = n;
 }
 
+// The per-workgroup LDS areas of a schedule (n_wg workgroups, n_chunks
+// split-KV chunks, batch sequences) on a device with lds_max bytes per
+// workgroup (0: unknown, no fitting).
+static KParams lds_plan(const mkd_config* c, int n_wg, int n_chunks, int batch, int lds_max) {
+  const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
+  KParams p{};
+  p.x_floats = x_floats_for(c, n_chunks, n_lm, batch);
+  p.out_floats = out_floats_for(c, n_wg, n_chunks, batch);
+  p.res_floats = res_floats_for(c, n_wg, n_chunks, batch);
+  p.d = c->d_model;
+  fit_x(p, c, n_chunks, n_lm, batch, lds_max);
+  set_pre(p, c, batch, lds_max);
+  return p;
+}
+
+int mkd_lds_plan(const mkd_config* cfg, int32_t batch, int32_t n_wg, int32_t n_chunks, int32_t lds_max,
+                 int32_t* out) {
+  const char* why = "";
+  if (!cfg || !out) return fail(MKD_E_INVALID, "null argument");
+  if (config_check(cfg, &why)) return fail(MKD_E_INVALID, why);
+  if (batch < 1 || batch > kMaxBatch || n_wg < 1 || n_chunks < 1 || n_chunks > 64 || lds_max < 0)
+    return fail(MKD_E_INVALID, "batch, n_wg, n_chunks or lds_max out of range");
+  const KParams p = lds_plan(cfg, n_wg, n_chunks, batch, lds_max);
+  out[0] = p.x_floats;
+  out[1] = p.out_floats;
+  out[2] = p.res_floats;
+  out[3] = p.pre_units;
+  out[4] = p.pre_off;
+  out[5] = (int32_t)lds_bytes(p);
+  return MKD_OK;
+}
+
 int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg) {
   if (!m) return fail(MKD_E_INVALID, "null model");
   if (n_cu) *n_cu = m->n_cu;
   if (max_coop_wg) {
-    KParams p{};
-    const int n_lm = m->cfg.vocab < m->n_cu ? m->cfg.vocab : m->n_cu;
-    p.x_floats = x_floats_for(&m->cfg, 1, n_lm, m->batch);
-    p.out_floats = out_floats_for(&m->cfg, m->n_cu, 1, m->batch);
-    p.res_floats = res_floats_for(&m->cfg, m->n_cu, 1, m->batch);
-    p.d = m->cfg.d_model;
     int lds_max = 0;
     hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
-    fit_x(p, &m->cfg, 1, n_lm, m->batch, lds_max);
-    set_pre(p, &m->cfg, m->batch, lds_max);
+    const KParams p = lds_plan(&m->cfg, m->n_cu, 1, m->batch, lds_max);
     int mx = 0;
     const int rc = max_coop_blocks(m->device, lds_bytes(p), m->batch, m->cfg.n_experts > 0, &mx);
     if (rc) return fail(rc, "occupancy query failed");
@@ -434,18 +459,10 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
     return fail(MKD_E_INVALID, "schedule is for " + std::to_string(batch) + " sequences, the model decodes " +
                                    std::to_string(m->batch));
   const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
-  const int x_floats = x_floats_for(c, n_chunks, n_lm, batch);
-  const int out_floats = out_floats_for(c, n_wg, n_chunks, batch);
-  const int res_floats = res_floats_for(c, n_wg, n_chunks, batch);
-  KParams p{};
-  p.x_floats = x_floats;
-  p.out_floats = out_floats;
-  p.res_floats = res_floats;
-  p.d = c->d_model;
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
-  fit_x(p, c, n_chunks, n_lm, batch, lds_max);
-  set_pre(p, c, batch, lds_max);
+  const KParams p = lds_plan(c, n_wg, n_chunks, batch, lds_max);
+  const int out_floats = p.out_floats, res_floats = p.res_floats;
   const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +

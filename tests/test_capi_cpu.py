@@ -124,6 +124,63 @@ def test_init_batch_rejects_batch_out_of_range_and_moe():
         assert e.value.code == code
 
 
+LDS_MAX = 160 * 1024   # bytes of LDS per workgroup on gfx950
+
+
+def _vec(n, batch):
+    """Floats of one interleaved input vector: 512-element segments, and with
+    several sequences 4 padding floats after every 8-element slice."""
+    padded = (n + 511) // 512 * 512
+    return padded if batch == 1 else padded // 8 * (8 * batch + 4)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_moe", "llama1b", "llama3b", "mixtral"])
+def test_lds_plan_invariants(name):
+    """The host's LDS layout: a full launch fits, and staged gate/up units never
+    overlap an input that is live while they are (several sequences: past the
+    O-projection and gate/up inputs inside the input area)."""
+    shape = synth.PRESETS[name]
+    c = capi.make_config(shape)
+    qd = shape.n_q_heads * shape.head_dim
+    batches = [1] if shape.n_experts else [1, 2, 3, 4, 5, 8]
+    for B in batches:
+        for n_wg in (256, 33, 7):
+            for n_chunks in (1, 4, 32):
+                p = capi.mkd_lds_plan(c, B, n_wg, n_chunks, LDS_MAX)
+                where = f"{name} B={B} n_wg={n_wg} n_chunks={n_chunks}: {p}"
+                # too few workgroups for a full-size model: the tiles' row
+                # results outgrow the LDS and loading the schedule fails
+                assert p["lds_bytes"] <= LDS_MAX or n_wg < 64, where
+                assert p["x_floats"] >= _vec(max(shape.d_model, qd), B), where
+                if shape.n_experts:
+                    assert p["pre_units"] == 0, where
+                if B == 1:
+                    assert p["pre_off"] == 0, where
+                elif p["pre_units"] > 0:
+                    assert p["pre_units"] >= 4 and p["pre_off"] % 4 == 0, where
+                    assert p["pre_off"] >= _vec(max(shape.d_model, qd), B), where
+                    assert p["pre_off"] + 8 * p["pre_units"] * 256 <= p["x_floats"], where
+                    # only while the down projection's input fits whole
+                    assert p["x_floats"] >= _vec(shape.d_ff, B), where
+
+
+def test_lds_plan_batched_staging_on_the_1b_shape():
+    """1B shape, 160 KiB: gate/up steps staged at B = 2 and 4; none at B = 8,
+    where the down projection runs in passes over K."""
+    c = capi.make_config(synth.PRESETS["llama1b"])
+    plan = {B: capi.mkd_lds_plan(c, B, 256, 1, LDS_MAX) for B in (1, 2, 4, 8)}
+    assert plan[1]["pre_units"] > 0 and plan[1]["pre_off"] == 0
+    assert plan[2]["pre_units"] == 16 and plan[4]["pre_units"] >= 12
+    assert plan[8]["pre_units"] == 0 and plan[8]["x_floats"] < _vec(8192, 8)
+    raw = capi.mkd_lds_plan(c, 4, 256, 1, 0)   # no device limit: the input area is not grown
+    assert raw["x_floats"] == _vec(8192, 4)
+    assert raw["pre_off"] + 8 * raw["pre_units"] * 256 <= raw["x_floats"]
+    for bad in ((0, 256, 1, LDS_MAX), (9, 256, 1, LDS_MAX), (2, 0, 1, LDS_MAX), (2, 256, 65, LDS_MAX),
+                (2, 256, 1, -1)):
+        with pytest.raises(capi.MkdError):
+            capi.mkd_lds_plan(c, *bad)
+
+
 def test_validator_rejects_mutations():
     cfg = synth.PRESETS["tiny"]
     c = capi.make_config(cfg)
