@@ -76,6 +76,30 @@ def test_tiny_batched_down_projection_in_passes(B, n_wg, n_chunks, monkeypatch):
     _check_against_oracle(cfg, starts, N, res, 0.1)
 
 
+def _random_shapes(n, seed=7):
+    """Seeded launch shapes: batch, grid size (1 to 256 workgroups), chunk count
+    and per-sequence start positions."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        B = rng.choice([2, 3, 4, 5, 6, 7, 8])
+        n_wg = rng.choice([1, 2, 5, 9, 17, 31, 48, 100, 128, 200, 255, 256])
+        n_chunks = rng.choice([1, 1, 2, 3, 5, 8])
+        out.append((B, n_wg, n_chunks, [rng.randrange(0, 150) for _ in range(B)]))
+    return out
+
+
+@pytest.mark.parametrize("B,n_wg,n_chunks,starts", _random_shapes(14))
+def test_tiny_batched_random_launch_shapes(B, n_wg, n_chunks, starts):
+    """Every batch size 2-8 over grids of 1 to 256 workgroups and 1 to 8 chunks:
+    ragged tiles, several instructions per workgroup, partial staging."""
+    require_gpu()
+    cfg = synth.PRESETS["tiny"]
+    res = _run_batched(cfg, starts, 3, n_wg, n_chunks, 0.1)
+    _check_against_oracle(cfg, starts, 3, res, 0.1)
+
+
 @pytest.mark.parametrize("B,n_wg", [(2, 7), (4, 256), (3, 33)])
 def test_tiny_batched_staged_gate_up_bit_exact(B, n_wg, monkeypatch):
     """Gate/up weight rows staged in LDS during the attention phase are consumed in
