@@ -161,6 +161,37 @@ def test_tiny_moe_kv_context(n_wg, n_chunks):
     assert ok, f"appended kv max err {mx}"
 
 
+def _random_shapes(n, seed=11):
+    """Seeded launch shapes: model, grid size (1 to 256 workgroups), chunk count
+    and start position."""
+    import random
+    rng = random.Random(seed)
+    return [(rng.choice(["tiny", "tiny_moe"]), rng.choice([1, 3, 6, 13, 40, 77, 128, 191, 250, 256]),
+             rng.choice([1, 1, 2, 3, 6, 8]), rng.randrange(0, 180)) for _ in range(n)]
+
+
+@pytest.mark.parametrize("name,n_wg,n_chunks,T0", _random_shapes(12))
+def test_tiny_random_launch_shapes(name, n_wg, n_chunks, T0):
+    """Batch-1 dense and MoE kernels over seeded grids of 1 to 256 workgroups and
+    1 to 8 chunks from random-filled caches: ragged tiles, several instructions
+    per workgroup, empty chunks at short contexts."""
+    cfg = synth.PRESETS[name]
+    N = 4
+    w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
+    say(f"{name} n_wg={n_wg} n_chunks={n_chunks} T0={T0}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab, stream=5)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    otoks, ologits, kv_o = oracle_run(cfg, w_cpu, synth.gen_kv_cache(cfg, T0 + N, T0), first, T0, N)
+    check_run(f"{name} n_wg={n_wg}", toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"
+
+
 @pytest.mark.timeout(900)
 def test_mixtral_full_size_kv1024():
     """Mixtral-shaped (93 GB of bf16 weights on the GPU), 2 steps.  The oracle
