@@ -121,26 +121,28 @@ class Weights:
     """Weight access by pointer-order index, converted to the oracle dtype.
 
     ``source(i)`` returns tensor ``i`` as anything ``np.asarray`` accepts after
-    ``.float()`` (a bf16 torch tensor); converted tensors are cached unless
-    ``cache=False`` (used for models larger than host memory).
+    ``.float()`` (a bf16 torch tensor).  Converted tensors are kept when
+    ``cache`` is true, or, when it is a function of the index, for the indices
+    it accepts (models larger than host memory keep only some tensors).
     """
 
-    def __init__(self, cfg, source: Callable[[int], object], dtype=np.float32, cache: bool = True):
+    def __init__(self, cfg, source: Callable[[int], object], dtype=np.float32, cache=True):
         import synth  # seeded inputs: names/shapes only
         self.cfg = cfg
         self.dtype = np.dtype(dtype)
         self.names = [n for n, _ in synth.weight_specs(cfg)]
         self.index = {n: i for i, n in enumerate(self.names)}
         self._source = source
-        self._cache = {} if cache else None
+        self._keep = cache if callable(cache) else (lambda i, c=bool(cache): c)
+        self._cache = {}
 
     def __call__(self, name: str) -> np.ndarray:
         i = self.index[name]
-        if self._cache is not None and i in self._cache:
+        if i in self._cache:
             return self._cache[i]
         t = self._source(i)
         a = np.asarray(t.float().cpu().numpy(), dtype=self.dtype)
-        if self._cache is not None:
+        if self._keep(i):
             self._cache[i] = a
         return a
 

@@ -9,5 +9,10 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    try:
+        from tests import gpu_common
+        gpu_common._capture = config.pluginmanager.getplugin("capturemanager")
+    except Exception:
+        pass
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")

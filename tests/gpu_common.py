@@ -11,8 +11,18 @@ from oracle import model as om
 ATOL, RTOL = 2e-2, 1e-2   # |gpu - oracle| <= ATOL + RTOL * |oracle|
 
 
+_capture = None   # pytest's capture manager, set by tests/conftest.py
+
+
 def say(*a):
-    print("[gpu-test]", *a, flush=True)
+    """Progress line, printed past pytest's output capture so that a long
+    test is seen to be alive."""
+    msg = " ".join(str(x) for x in ("[gpu-test]",) + a)
+    if _capture is not None:
+        with _capture.global_and_fixture_disabled():
+            print(msg, flush=True)
+    else:
+        print(msg, flush=True)
     sys.stdout.flush()
 
 

@@ -1,0 +1,168 @@
+"""GPU parity over whole decode runs of every full-size workload.
+
+Each run decodes the workload's full step count in one launch (128 greedy
+steps for the Llama-3.2-1B/3B shapes, 64 for the 1B long-context caches, as
+many as the time budget allows for the Mixtral shape) and compares every
+step's logits with the CPU oracle's, element by element, with 100% greedy
+agreement required over the run.  A fused kernel that drifts numerically over
+many steps is the failure these runs are for (Hyperkernel teardown, "Which
+claims the repo backs": agreement with a reference over whole decodes is what
+the released kernels are judged by).
+
+The oracle gets its own copy of the seeded inputs from the host generator
+(Mixtral: too large for host memory as fp32, so each weight is read back from
+the generated device tensors, which the generator makes bit-identical to the
+host's; one tensor is spot-checked).  Weights are generated once per model and
+shared by that model's runs.
+"""
+import gc
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import model as om
+from persistent_megakernel_decode_02_amd.decoder import Decoder
+from persistent_megakernel_decode_02_amd.tuning import launch_config
+from tests.gpu_common import check_run, close_enough, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+_models = {}
+
+
+def _model(name):
+    """(device weights, oracle weights) of a preset; one preset is kept at a time."""
+    if name not in _models:
+        _models.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        cfg = synth.PRESETS[name]
+        t = time.time()
+        w_gpu = synth.gen_weights(cfg, device="cuda")
+        torch.cuda.synchronize()
+        w_cpu = synth.gen_weights(cfg, device="cpu")
+        say(f"{name}: weights generated on both devices in {time.time() - t:.1f}s")
+        _models[name] = (w_gpu, om.Weights.from_list(cfg, w_cpu))
+    return _models[name]
+
+
+def _full_run(name, T0, N, n_chunks=None):
+    require_gpu()
+    cfg = synth.PRESETS[name]
+    w_gpu, w_orc = _model(name)
+    max_seq = T0 + N
+    kv_gpu = synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")
+    torch.cuda.synchronize()
+    n_wg, nc = launch_config(cfg, T0, N)
+    n_chunks = n_chunks or nc
+    say(f"{name} T0={T0} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, max_seq, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab)[0]
+    t = time.time()
+    toks, logits = dec.decode(first, T0, N)
+    say(f"gpu run {time.time() - t:.2f}s")
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    kv_pre_same = torch.equal(kv_gpu[:, :, :, :T0], synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")[:, :, :, :T0])
+    dec.close()
+    del kv_gpu
+    torch.cuda.empty_cache()
+    assert kv_pre_same, "the kernel changed cache positions before the start position"
+    orc = om.Oracle(cfg, w_orc)
+    kv_o = om.kv_to_oracle(synth.gen_kv_cache(cfg, max_seq, T0))
+    t = time.time()
+    otoks, ologits = orc.decode(first, T0, N, kv_o)
+    say(f"oracle {N} steps in {time.time() - t:.1f}s")
+    check_run(f"{name}@{T0} x{N}", toks, logits, otoks, ologits)
+    ok, mx, nbad = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    say(f"appended kv max|err| {mx:.3e}")
+    assert ok, f"appended kv: {nbad} values outside tolerance (max err {mx})"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T0", [128, 1024, 4096])
+def test_llama1b_128_steps(T0):
+    _full_run("llama1b", T0, 128)
+
+
+@pytest.mark.timeout(900)
+def test_llama1b_kv1024_16_chunks():
+    """split-KV at a context where the launch shape would not split (one
+    chunk): the reduction stage at 16 chunks over 32 steps"""
+    _full_run("llama1b", 1024, 32, n_chunks=16)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T0", [16384, 32768])
+def test_llama1b_long_context_64_steps(T0):
+    _full_run("llama1b", T0, 64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T0", [128, 2048])
+def test_llama3b_128_steps(T0):
+    _full_run("llama3b", T0, 128)
+
+
+MIXTRAL_STEPS = 16
+
+
+@pytest.mark.timeout(900)
+def test_mixtral_kv1024():
+    """Mixtral-shaped (93 GB of bf16 weights on the GPU) from a 1024-position
+    cache, MIXTRAL_STEPS greedy steps.  The oracle keeps every tensor but the
+    experts in host memory and reads the two routed experts of each layer
+    back from the device tensors per use."""
+    require_gpu()
+    _models.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+    cfg = synth.PRESETS["mixtral"]
+    T0, N = 1024, MIXTRAL_STEPS
+    say("mixtral: generating 93 GB of weights on the GPU")
+    t = time.time()
+    w_gpu = []
+    for i in range(len(synth.weight_specs(cfg))):
+        w_gpu.append(synth.gen_weights(cfg, device="cuda", only=[i])[i])
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+            say(f"  tensor {i}")
+    kv_gpu = synth.gen_kv_cache(cfg, T0 + N, T0, device="cuda")
+    torch.cuda.synchronize()
+    say(f"mixtral: generated in {time.time() - t:.1f}s")
+    n_wg, n_chunks = launch_config(cfg, T0, N)
+    say(f"mixtral T0={T0} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    del kv_gpu
+    probe = synth.gen_weights(cfg, device="cpu", only=[4])[4]
+    assert torch.equal(probe, w_gpu[4].cpu())
+    names = [n for n, _ in synth.weight_specs(cfg)]
+    expert = [(".gate." in n or ".up." in n or ".down." in n) for n in names]
+    orc = om.Oracle(cfg, om.Weights(cfg, lambda i: w_gpu[i], cache=lambda i: not expert[i]))
+    kv_o = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + N, T0))
+    t = time.time()
+    # in pieces of 4 greedy steps (each piece starts from the argmax of the
+    # previous piece's last step, as the next step of one run would), so that
+    # progress is reported while the oracle reads the experts back
+    otoks, ologits, tok = [], [], first
+    for s0 in range(0, N, 4):
+        tk, lg = orc.decode(tok, T0 + s0, min(4, N - s0), kv_o)
+        otoks += tk
+        ologits.append(lg)
+        tok = tk[-1]
+        say(f"mixtral: oracle {len(otoks)}/{N} steps, {time.time() - t:.1f}s")
+    ologits = np.concatenate(ologits)
+    del w_gpu, orc
+    gc.collect()
+    torch.cuda.empty_cache()
+    check_run(f"mixtral@{T0} x{N}", toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"

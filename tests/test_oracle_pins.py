@@ -374,6 +374,31 @@ def test_incremental_decode_equals_prefill(cfg):
     assert np.array_equal(kv_a, kv_b)
 
 
+@pytest.mark.parametrize("cfg,std,seed", [(synth.PRESETS["tiny"], 0.02, 2), (MICRO_MOE, 0.5, 2),
+                                          (MICRO_TIED, 0.5, 8)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_greedy_decode_feeds_each_argmax_to_the_next_step(cfg, std, seed):
+    """The free-running branch of Oracle.decode: step i consumes the argmax of
+    step i-1.  A causal prefill over [first] + tokens[:-1] -- no incremental
+    cache and no token feed of its own -- must give every step's logits, and
+    each row's argmax must be the token decode returned for that step.  The
+    run must visit several tokens, so that feeding the wrong step's token
+    (an off-by-one) would change the logits."""
+    ws = synth.gen_weights(cfg, seed=seed, gain_std=0.1, std=std)
+    n = 12
+    first = synth.gen_tokens(1, cfg.vocab, stream=4)[0]
+    orc = om.Oracle(cfg, om.Weights.from_list(cfg, ws, dtype=np.float64))
+    kv_a = np.zeros((cfg.n_layers, 2, cfg.n_kv_heads, n, cfg.head_dim))
+    toks, logits = orc.decode(first, 0, n, kv_a)
+    assert len(set(toks)) >= 4, f"degenerate greedy run {toks}"
+    assert any(a != b for a, b in zip(toks, toks[1:]))
+    kv_b = np.zeros_like(kv_a)
+    pre = orc.prefill([first] + toks[:-1], kv_b)
+    assert np.allclose(pre, logits, rtol=1e-9, atol=1e-9)
+    assert [int(np.argmax(r)) for r in pre] == toks
+    assert np.array_equal(kv_a, kv_b)
+
+
 def test_fp32_oracle_within_noise_floor_of_fp64():
     cfg = synth.PRESETS["tiny"]
     ws = synth.gen_weights(cfg, seed=0)
