@@ -18,11 +18,15 @@
  *     Nothing throws across the ABI; mkd_last_error() gives a message for
  *     the calling thread's last failure.
  *   - Pointers marked "device" are GPU memory on the model's device; "host"
- *     pointers are CPU memory.  Weights, KV cache and outputs are owned by
- *     the caller and only borrowed; the library allocates (hipMalloc) its own
- *     small buffers (schedule, tagged activations, RoPE table, status) and
- *     frees them in mkd_destroy.
+ *     pointers are CPU memory.  All memory is the caller's and only
+ *     borrowed: weights, KV cache, outputs, a device workspace (sized by
+ *     mkd_workspace_bytes; it holds the pointer table, RoPE table, status
+ *     words, schedule and tagged activations) and a small pinned host control
+ *     block (the stop word).  The library allocates no device or pinned
+ *     memory of its own; a handle is a small host object.
  *   - Streams are passed as void* (a hipStream_t; NULL = default stream).
+ *   - Functions marked "plumbing" are library housekeeping that no page
+ *     describes; every other declaration names the passage it follows.
  */
 #ifndef MKD_H
 #define MKD_H
@@ -34,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MKD_ABI_VERSION 2
+#define MKD_ABI_VERSION 3
 
 enum {
   MKD_OK = 0,
@@ -83,21 +87,27 @@ typedef struct mkd_status {
 
 typedef struct mkd_model mkd_model;
 
-/* MKD_ABI_VERSION of the loaded library. */
+/* MKD_ABI_VERSION of the loaded library.  Plumbing. */
 int mkd_version(void);
 
 /* Message of the calling thread's last error ("" if none).  The pointer
- * stays valid until the thread's next library call. */
+ * stays valid until the thread's next library call.  Plumbing. */
 const char* mkd_last_error(void);
 
 /* Check a configuration against the limits above.  MKD_E_INVALID with a
- * message if it is outside them. */
+ * message if it is outside them: the kernels are specialised for these
+ * shapes and refuse others, as the released megakernels refuse shapes they
+ * were not built for (Hyperkernel teardown, "What is in the repository":
+ * one kernel per exact shape, and the host rejects any other). */
 int mkd_config_check(const mkd_config* cfg);
 
-/* Number of weight tensors mkd_init expects for cfg. */
+/* Number of weight tensors mkd_init expects for cfg (the model is initialised
+ * from weight pointers, Hyperkernel teardown, "What is in the repository":
+ * the host places each checkpoint tensor where the plan says). */
 int mkd_weight_count(const mkd_config* cfg, size_t* n_out);
 
-/* Shape of weight tensor `index` in the fixed pointer order:
+/* Shape of weight tensor `index` in the fixed pointer order (the plan's
+ * tensor map, Hyperkernel teardown, "What is in the repository"):
  *   embed [V, d], final_norm [d], lm_head [V, d] (only when untied), then per
  *   layer attn_norm [d], wq [hq*hd, d], wk [hkv*hd, d], wv [hkv*hd, d],
  *   wo [d, hq*hd], ffn_norm [d], and either w_gate [F, d], w_up [F, d],
@@ -107,7 +117,9 @@ int mkd_weight_count(const mkd_config* cfg, size_t* n_out);
 int mkd_weight_shape(const mkd_config* cfg, size_t index, int64_t* rows, int64_t* cols);
 
 /* Bytes of the KV cache for max_seq positions:
- * bf16 [n_layers][2 (K, V)][n_kv_heads][max_seq][head_dim]. */
+ * bf16 [n_layers][2 (K, V)][n_kv_heads][max_seq][head_dim].  Each head's
+ * positions are contiguous, so a split-KV chunk is one linear stream (the
+ * decode attention the Kittens VM summary's "Results" times). */
 int mkd_kv_cache_bytes(const mkd_config* cfg, int32_t max_seq, size_t* bytes_out);
 
 /* Build the instruction tensor (schedule spec v4, one sequence) on the host,
@@ -133,32 +145,75 @@ int mkd_schedule_build_batch(const mkd_config* cfg, int32_t n_wg, int32_t n_chun
 
 /* Check a schedule tensor's invariants (ranges, every row of every stage
  * produced exactly once, waits naming the producing stage, lists in stage
- * order).  MKD_OK or MKD_E_INVALID with a message. */
+ * order): the "barrier that does not deadlock" and "schedule that keeps every
+ * SM busy" the Hyperkernel teardown names as the hard parts ("What a
+ * megakernel buys").  MKD_OK or MKD_E_INVALID with a message. */
 int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_words);
 
-/* Create a model handle on `device`.
+/* Split-KV chunk count the library uses when a schedule leaves it to it
+ * (n_chunks = 0): one chunk up to 512 KiB of K and V per KV head at
+ * n_positions, else one chunk per workgroup and KV head (at most 64).  The
+ * split itself is the decode-attention split of the Kittens VM summary
+ * ("Results": a split-KV decode kernel at small batch); the rule is this
+ * library's measured choice.  Host only.  MKD_E_INVALID for a bad argument. */
+int mkd_default_chunks(const mkd_config* cfg, int32_t n_wg, int32_t n_positions, int32_t* n_chunks);
+
+/* Bytes of device workspace a handle needs to run schedules of n_wg
+ * workgroups and n_chunks split-KV chunks (0: mkd_default_chunks at
+ * max_seq) for `batch` sequences and positions [0, max_seq).  The host
+ * writes its tables to the addresses its plan names inside this memory
+ * (Hyperkernel teardown, "What is in the repository").  Host only.
+ * MKD_E_INVALID for a bad argument. */
+int mkd_workspace_bytes(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch, int32_t max_seq,
+                        size_t* bytes_out);
+
+/* Byte offsets of the workspace regions for the same arguments, into the
+ * caller's offsets_out[8]: pointer table, RoPE table, status words, zero
+ * page, schedule, tagged activation block, completion flags (inside the
+ * activation block), and the total (= mkd_workspace_bytes).  Every region
+ * starts on a 256-byte boundary.  Host only; the plan's memory map
+ * (Hyperkernel teardown, "What is in the repository"). */
+int mkd_workspace_layout(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch, int32_t max_seq,
+                         size_t* offsets_out);
+
+/* Create a model handle on `device` from weight pointers (the host places
+ * tensors where the plan says and the model's knowledge stays in the kernel
+ * and the plan, Hyperkernel teardown, "What is in the repository").
  * weights: host array of n_weights device pointers (bf16, 16-byte aligned,
  *   order and shapes as in mkd_weight_shape).
  * kv_cache: device, bf16, mkd_kv_cache_bytes(cfg, max_seq) bytes.
- * Computes the RoPE cos/sin table (fp64 angles rounded to fp32) for
- * positions [0, max_seq) and uploads it with the pointer table.
- * Errors: MKD_E_INVALID (shape, null or misaligned pointer, count),
- * MKD_E_HIP, MKD_E_UNSUPPORTED (device is not gfx950-class or lacks
- * cooperative launch). */
+ * workspace: device memory of `device`, 256-byte aligned, workspace_bytes
+ *   long; at least the tables' part of mkd_workspace_bytes (each schedule
+ *   loaded later checks that it fits as a whole).  Init writes the pointer
+ *   table, the RoPE cos/sin table (fp64 angles rounded to fp32) for positions
+ *   [0, max_seq), the status words and a zero page into it.
+ * host_control: pinned host memory mapped for the device (hipHostMalloc, or
+ *   a torch tensor made with pin_memory=True), 16 int32 words, 64-byte
+ *   aligned; word 0 is the stop word of mkd_abort.  Init zeroes it.
+ * Everything is borrowed: the caller keeps it alive until mkd_destroy.
+ * Errors: MKD_E_INVALID (shape, null, misaligned or wrong-kind pointer,
+ * count, workspace too small), MKD_E_HIP, MKD_E_UNSUPPORTED (device is not
+ * gfx950-class or lacks cooperative launch). */
 int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights,
-             void* kv_cache, int32_t max_seq, int32_t device, mkd_model** out);
+             void* kv_cache, int32_t max_seq, void* workspace, size_t workspace_bytes,
+             int32_t* host_control, int32_t device, mkd_model** out);
 
 /* As mkd_init, for `batch` sequences (1..8) decoded together by
  * mkd_decode_batch.  kv_cache holds `batch` caches one after the other:
  * batch * mkd_kv_cache_bytes(cfg, max_seq) bytes, sequence b's cache at byte
  * b * mkd_kv_cache_bytes(cfg, max_seq).  Dense models only for batch > 1
  * (MKD_E_UNSUPPORTED for MoE: each sequence would route to its own experts).
- * Schedules built or loaded for the handle must have the same batch. */
+ * Schedules built or loaded for the handle must have the same batch.  No
+ * page describes a batched megakernel; the Kittens VM summary ("Results")
+ * quotes a decode figure of a related kernel at a 4-prompt batch. */
 int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights,
-                   void* kv_cache, int32_t max_seq, int32_t batch, int32_t device, mkd_model** out);
+                   void* kv_cache, int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes,
+                   int32_t* host_control, int32_t device, mkd_model** out);
 
 /* Query the device's compute-unit count and the largest grid a cooperative
- * launch of the megakernel can hold on it. */
+ * launch of the megakernel can hold on it: one block per compute unit, all
+ * resident at once, as a grid-wide wait requires (Hyperkernel teardown,
+ * "What is in the repository": cooperative launches of one block per SM). */
 int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg);
 
 /* Host-only query (no device needed): the LDS areas, in floats, that a
@@ -176,17 +231,24 @@ int mkd_lds_plan(const mkd_config* cfg, int32_t batch, int32_t n_wg, int32_t n_c
                  int32_t* out);
 
 /* Build (as mkd_schedule_build) and upload the schedule the next launches
- * use; n_wg = 0 means one workgroup per compute unit; n_chunks = 0 picks a
- * split so that each chunk covers about 32 KiB of K and V at the handle's
- * max_seq.  host_out / capacity / n_words as in mkd_schedule_build (host_out
- * may be NULL).  MKD_E_COOPERATIVE if n_wg exceeds what can be co-resident. */
+ * use into the workspace (the host-built schedule of every operation,
+ * Hyperkernel teardown, "What a megakernel buys"); n_wg = 0 means one
+ * workgroup per compute unit; n_chunks = 0 takes mkd_default_chunks at the
+ * handle's max_seq.  host_out / capacity / n_words as in mkd_schedule_build
+ * (host_out may be NULL).  MKD_E_COOPERATIVE if n_wg exceeds what can be
+ * co-resident; MKD_E_INVALID if the schedule and its activations do not fit
+ * in the handle's workspace. */
 int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks,
                        int32_t* host_out, size_t capacity, size_t* n_words);
 
-/* Upload a schedule built elsewhere (validated first). */
+/* Upload a schedule built elsewhere (validated first, then as
+ * mkd_build_schedule; Hyperkernel teardown, "What a megakernel buys"). */
 int mkd_load_schedule(mkd_model* m, const int32_t* words, size_t n_words);
 
-/* Enqueue ONE cooperative launch that decodes n_steps tokens on `stream`.
+/* Enqueue ONE cooperative launch that decodes n_steps tokens on `stream`
+ * (one launch per call, Hyperkernel teardown, "A single kernel launch, read
+ * from the host"; the blocks never exit between tokens, "What a megakernel
+ * buys").
  * Step i consumes a token at position start_pos + i: first_token for i = 0,
  * otherwise forced_dev[i] when forced_dev is non-NULL and forced_dev[i] >= 0,
  * otherwise the argmax (lowest index on ties) of step i-1's logits.  Step i
@@ -198,7 +260,8 @@ int mkd_load_schedule(mkd_model* m, const int32_t* words, size_t n_words);
  * Asynchronous: returns after enqueueing; use mkd_wait for the outcome.
  * Errors (host-side checks): MKD_E_INVALID (no schedule, first_token not in
  * [0, vocab), start_pos < 0, n_steps < 1, start_pos + n_steps > max_seq,
- * NULL tokens_out_dev), MKD_E_COOPERATIVE, MKD_E_HIP. */
+ * NULL tokens_out_dev, the handle's previous launch still running),
+ * MKD_E_COOPERATIVE, MKD_E_HIP.  Clears the stop word before it enqueues. */
 int mkd_decode(mkd_model* m, int32_t first_token, int32_t start_pos, int32_t n_steps,
                const int32_t* forced_dev, int32_t* tokens_out_dev, float* logits_out_dev,
                void* stream);
@@ -224,15 +287,22 @@ int mkd_decode_batch(mkd_model* m, const int32_t* first_tokens, const int32_t* s
  * MKD_E_WATCHDOG, MKD_E_BOUNDS, MKD_E_NONFINITE, MKD_E_ABORTED. */
 int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out);
 
-/* Ask running launches to stop: sets the stop word (pinned host memory) that
- * every device-side wait polls.  Cleared by the next mkd_wait that completes. */
+/* Ask the handle's running launch to stop: sets the stop word (word 0 of the
+ * host control block) that every device-side wait polls; the launch then
+ * ends with MKD_E_ABORTED (Hyperkernel teardown, "Hardware fault detection
+ * and replanning": a stop word in the kernel's control block).  No effect
+ * when no launch is in flight.  mkd_wait and the next launch clear it. */
 int mkd_abort(mkd_model* m);
 
 /* Device-side deadline, in milliseconds, for any single wait of a workgroup
- * on another's output (default 2000).  Must be >= 1. */
+ * on another's output (default 2000).  Must be >= 1.  The watchdog word of
+ * the control block (Hyperkernel teardown, "Hardware fault detection and
+ * replanning"); the launch then ends with MKD_E_WATCHDOG. */
 int mkd_set_watchdog(mkd_model* m, int32_t watchdog_ms);
 
-/* Per-instruction timestamps: when trace_dev is non-NULL, each launch writes,
+/* Per-instruction timestamps, to account for each opcode's cost (the
+ * epic-kernel README's profiling build and its HBM-utilisation plot): when
+ * trace_dev is non-NULL, each launch writes,
  * for instruction i of workgroup wg at decode step `step`, four words at
  * trace_dev[((wg * n_steps + step) * max_instr + i) * 4]: wall-clock ticks
  * when the instruction starts, when its inputs are ready, and when it has
@@ -244,14 +314,37 @@ int mkd_set_trace(mkd_model* m, uint64_t* trace_dev, size_t capacity_words);
 /* Duration in milliseconds of the last launch's megakernel alone, from HIP
  * events recorded on its stream just before and after the cooperative kernel
  * (the small buffer-reset kernel that precedes it is outside the interval).
- * Call after mkd_wait.  MKD_E_INVALID if nothing has run. */
+ * Call after mkd_wait.  MKD_E_INVALID if nothing has run.  The time that
+ * the weight-read floor is set against (Hyperkernel teardown, "Where the
+ * numbers sit against the hardware"). */
 int mkd_kernel_ms(mkd_model* m, float* ms);
 
-/* Wall-clock tick rate of the device in Hz (for trace and watchdog). */
+/* Wall-clock tick rate of the device in Hz (for trace and watchdog).
+ * Plumbing. */
 int mkd_clock_hz(mkd_model* m, double* hz);
 
-/* Free the handle and the library's own buffers (not the borrowed ones).
- * Waits for outstanding launches first.  NULL is a no-op. */
+/* Limits on the per-workgroup LDS plan of schedules built or loaded after
+ * this call: the batched input area in floats (0 = no limit; rounded down to
+ * whole 512-element segments of every sequence, and never below what the
+ * normalised inputs need) and the staged gate/up weight units per wavefront
+ * (-1 = no limit).  They only shrink what the plan would use, so that tests
+ * can reach the down projection's passes over K on small models and compare
+ * staged with unstaged launches; the staging itself is the next
+ * instruction's weights loaded ahead of it (epic-kernel README, "L2
+ * prefetching overlapped with prior instructions").  MKD_E_INVALID for
+ * negative limits (other than -1 for the units). */
+int mkd_set_lds_limits(mkd_model* m, int32_t max_input_floats, int32_t max_staged_units);
+
+/* cooperative = 1 (the default): launches are cooperative, so the runtime
+ * guarantees the whole grid is resident, as a grid-wide wait needs
+ * (Hyperkernel teardown, "What is in the repository").  0: the same grid is
+ * dispatched plainly, for profilers that cannot finish their output after a
+ * cooperative dispatch; the grid was checked to fit co-resident, so on an
+ * idle device it is resident either way.  MKD_E_INVALID otherwise. */
+int mkd_set_launch_mode(mkd_model* m, int32_t cooperative);
+
+/* Free the handle (not the borrowed memory).  Waits for an outstanding
+ * launch first.  NULL is a no-op.  Plumbing. */
 void mkd_destroy(mkd_model* m);
 
 #ifdef __cplusplus

@@ -1,7 +1,7 @@
 """Build libmkd.so (HIP for gfx950 + host C++) in-tree.
 
-Usage: ``python -m persistent_megakernel_decode_02_amd.build`` (always
-recompiles).  Objects go to ``_build/`` at the repository root; the shared
+Usage: ``python -m persistent_megakernel_decode_02_amd.build`` (recompiles
+everything; ``--incremental`` only what changed).  Objects go to ``_build/`` at the repository root; the shared
 library lands next to this file, where the binding loads it.
 """
 from __future__ import annotations
@@ -30,37 +30,68 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-I" + os.path.join(ROCM, "include")]
 
 
-def _run(cmd):
-    t = time.time()
-    r = subprocess.run(cmd, capture_output=True, text=True)
+# device translation units (each kernel on its own, so they compile in
+# parallel) and host ones; every object depends on the headers too
+DEVICE_SRCS = ["mkd_kernel_dense.hip", "mkd_kernel_moe.hip", "mkd_kernel_batch.hip", "mkd_launch.hip"]
+HOST_SRCS = ["mkd_api.cpp", "schedule.cpp"]
+HEADERS = [os.path.join(CSRC, "mkd_device.h"), os.path.join(CSRC, "mkd_internal.h"),
+           os.path.join(INCLUDE, "mkd.h")]
+
+
+def _steps():
+    steps = []
+    for src in DEVICE_SRCS:
+        steps.append(([HIPCC] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src)], src, src.rsplit(".", 1)[0] + ".o"))
+    steps.append(([HIPCC] + HOST_FLAGS + ["-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
+                                          os.path.join(CSRC, "mkd_api.cpp")], "mkd_api.cpp", "mkd_api.o"))
+    steps.append((["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "schedule.cpp")], "schedule.cpp", "schedule.o"))
+    return steps
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(f) > t for f in [os.path.join(CSRC, src)] + HEADERS)
+
+
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every translation unit (in parallel) and link libmkd.so.
+    incremental=True recompiles only objects older than their sources."""
+    os.makedirs(BUILD, exist_ok=True)
+    procs, objs = [], []
+    t0 = time.time()
+    for cmd, src, obj in _steps():
+        out = os.path.join(BUILD, obj)
+        objs.append(out)
+        if incremental and not _stale(src, out):
+            continue
+        tmp = out + ".tmp.o"
+        procs.append((obj, out, tmp, cmd, subprocess.Popen(cmd + ["-o", tmp], stdout=subprocess.PIPE,
+                                                            stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for obj, out, tmp, cmd, pr in procs:
+        log, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(log)
+            failed.append(obj)
+            continue
+        os.replace(tmp, out)
+        if verbose:
+            print(f"[build] {obj} ({time.time() - t0:.1f}s)", flush=True)
+    if failed:
+        raise RuntimeError("build failed: " + ", ".join(failed))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
+                       capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("build step failed: " + " ".join(cmd))
-    return time.time() - t
-
-
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    steps = [
-        ([HIPCC] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, "mkd_kernel.hip")], "mkd_kernel.o"),
-        ([HIPCC] + HOST_FLAGS + ["-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
-                                 os.path.join(CSRC, "mkd_api.cpp")], "mkd_api.o"),
-        (["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "schedule.cpp")], "schedule.o"),
-    ]
-    for cmd, obj in steps:
-        out = os.path.join(BUILD, obj)
-        dt = _run(cmd + ["-o", out])
-        objs.append(out)
-        if verbose:
-            print(f"[build] {obj} ({dt:.1f}s)", flush=True)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
+        raise RuntimeError("link failed")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"[build] {LIB}", flush=True)
+        print(f"[build] {LIB} ({time.time() - t0:.1f}s)", flush=True)
     return LIB
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)

@@ -34,10 +34,16 @@ OPCODE_NAMES = {1: "QKV", 2: "ATTN", 3: "AREDUCE", 4: "OPROJ", 5: "UPGATE", 6: "
 # every function include/mkd.h declares
 EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_count",
            "mkd_weight_shape", "mkd_kv_cache_bytes", "mkd_schedule_build",
-           "mkd_schedule_build_batch", "mkd_schedule_validate", "mkd_init", "mkd_init_batch",
+           "mkd_schedule_build_batch", "mkd_schedule_validate", "mkd_default_chunks",
+           "mkd_workspace_bytes", "mkd_workspace_layout", "mkd_init", "mkd_init_batch",
            "mkd_device_info", "mkd_lds_plan", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
            "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
-           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_destroy")
+           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_set_lds_limits",
+           "mkd_set_launch_mode", "mkd_destroy")
+
+# regions of a workspace, in mkd_workspace_layout's order
+WORKSPACE_REGIONS = ("wtab", "rope", "status", "zero", "schedule", "activations", "flags", "total")
+CONTROL_WORDS = 16   # int32 words of the pinned host control block
 
 
 class mkd_config(ctypes.Structure):
@@ -87,8 +93,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_schedule_build": ([cfgp, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_schedule_build_batch": ([cfgp, I32, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
         "mkd_schedule_validate": ([cfgp, P, SZ], ctypes.c_int),
-        "mkd_init": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
-        "mkd_init_batch": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, I32, ctypes.POINTER(P)], ctypes.c_int),
+        "mkd_default_chunks": ([cfgp, I32, I32, ctypes.POINTER(I32)], ctypes.c_int),
+        "mkd_workspace_bytes": ([cfgp, I32, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "mkd_workspace_layout": ([cfgp, I32, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "mkd_init": ([cfgp, ctypes.POINTER(P), SZ, P, I32, P, SZ, P, I32, ctypes.POINTER(P)], ctypes.c_int),
+        "mkd_init_batch": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, P, SZ, P, I32, ctypes.POINTER(P)],
+                           ctypes.c_int),
         "mkd_device_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_lds_plan": ([cfgp, I32, I32, I32, I32, ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_build_schedule": ([P, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
@@ -101,6 +111,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_set_trace": ([P, P, SZ], ctypes.c_int),
         "mkd_kernel_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mkd_clock_hz": ([P, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "mkd_set_lds_limits": ([P, I32, I32], ctypes.c_int),
+        "mkd_set_launch_mode": ([P, I32], ctypes.c_int),
         "mkd_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
@@ -185,22 +197,39 @@ def mkd_schedule_validate(cfg: mkd_config, words: np.ndarray) -> None:
     _check(load().mkd_schedule_validate(ctypes.byref(cfg), w.ctypes.data, w.size))
 
 
-def mkd_init(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, device: int = 0) -> int:
-    """Handle (an int) for device tensors ``weights`` (pointer order) and ``kv_cache``."""
-    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
-    h = ctypes.c_void_p()
-    _check(load().mkd_init(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, device,
-                           ctypes.byref(h)))
-    return h.value
+def mkd_default_chunks(cfg: mkd_config, n_wg: int, n_positions: int) -> int:
+    n = ctypes.c_int32()
+    _check(load().mkd_default_chunks(ctypes.byref(cfg), n_wg, n_positions, ctypes.byref(n)))
+    return n.value
 
 
-def mkd_init_batch(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, batch: int,
-                   device: int = 0) -> int:
+def mkd_workspace_bytes(cfg: mkd_config, n_wg: int, n_chunks: int, batch: int, max_seq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().mkd_workspace_bytes(ctypes.byref(cfg), n_wg, n_chunks, batch, max_seq, ctypes.byref(n)))
+    return n.value
+
+
+def mkd_workspace_layout(cfg: mkd_config, n_wg: int, n_chunks: int, batch: int, max_seq: int) -> dict:
+    out = (ctypes.c_size_t * len(WORKSPACE_REGIONS))()
+    _check(load().mkd_workspace_layout(ctypes.byref(cfg), n_wg, n_chunks, batch, max_seq, out))
+    return dict(zip(WORKSPACE_REGIONS, list(out)))
+
+
+def mkd_init(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, workspace, control,
+             device: int = 0) -> int:
+    """Handle (an int) for device tensors ``weights`` (pointer order), ``kv_cache`` and
+    ``workspace`` (uint8) and the pinned host tensor ``control`` (int32[16])."""
+    return mkd_init_batch(cfg, weights, kv_cache, max_seq, 1, workspace, control, device)
+
+
+def mkd_init_batch(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, batch: int, workspace,
+                   control, device: int = 0) -> int:
     """As mkd_init for ``batch`` sequences; ``kv_cache`` holds every sequence's cache."""
     arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
     h = ctypes.c_void_p()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().mkd_init_batch(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, batch,
-                                 device, ctypes.byref(h)))
+                                 _ptr(workspace), nbytes, _ptr(control), device, ctypes.byref(h)))
     return h.value
 
 
@@ -288,6 +317,14 @@ def mkd_clock_hz(m: int) -> float:
     hz = ctypes.c_double()
     _check(load().mkd_clock_hz(m, ctypes.byref(hz)))
     return hz.value
+
+
+def mkd_set_lds_limits(m: int, max_input_floats: int = 0, max_staged_units: int = -1) -> None:
+    _check(load().mkd_set_lds_limits(m, max_input_floats, max_staged_units))
+
+
+def mkd_set_launch_mode(m: int, cooperative: bool) -> None:
+    _check(load().mkd_set_launch_mode(m, 1 if cooperative else 0))
 
 
 def mkd_destroy(m: int) -> None:

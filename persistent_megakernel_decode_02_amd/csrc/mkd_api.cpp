@@ -36,6 +36,18 @@ size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 }  // namespace
 
+// Byte layout of a handle's workspace (caller-owned device memory).  The
+// tables init writes come first; the schedule and the tagged activation block
+// of the loaded schedule follow.  Every region starts on a 256-byte boundary.
+struct WsLayout {
+  size_t wtab = 0, rope = 0, status = 0, zero = 0, fixed = 0;  // written by init
+  size_t sched = 0, ll = 0, total = 0;                          // per schedule
+  size_t sched_words = 0, ll_words = 0;
+  int flag_stride = 0;
+  size_t sz[9] = {};  // words of h, qkv, part, aout, hmid, act, route, lm, flags
+  int32_t s_qkv = 0, s_part = 0;
+};
+
 struct mkd_model {
   mkd_config cfg{};
   int device = 0;
@@ -43,23 +55,29 @@ struct mkd_model {
   int32_t max_seq = 0;
   uint16_t* kv = nullptr;
   std::vector<uint64_t> wptr;
-  uint64_t* d_wtab = nullptr;
+  char* ws = nullptr;            // borrowed workspace
+  size_t ws_bytes = 0;
+  WsLayout lay;
+  uint64_t* d_wtab = nullptr;    // regions of the workspace
   float* d_rope = nullptr;
   int32_t* d_status = nullptr;
-  void* d_zero = nullptr;   // 4 KiB of zeros: streamer loads past the end of a tile
-  int32_t* h_stop = nullptr;
+  void* d_zero = nullptr;        // 4 KiB of zeros: streamer loads past the end of a tile
+  int32_t* h_ctrl = nullptr;     // borrowed pinned host control block; word 0 = stop
+  const int32_t* d_stop = nullptr;  // its device-side address
   uint64_t* d_ll = nullptr;
-  size_t ll_words = 0, ll_cap = 0;
+  size_t ll_words = 0;
   // sub-buffers of d_ll
   uint64_t *h = nullptr, *qkv = nullptr, *part = nullptr, *aout = nullptr, *hmid = nullptr,
            *act = nullptr, *route = nullptr, *lm = nullptr, *flags = nullptr;
   int32_t* d_sched = nullptr;
-  size_t sched_words = 0, sched_cap = 0;
+  size_t sched_words = 0;
   int batch = 1;  // sequences decoded together
   int n_wg = 0, n_chunks = 0, max_instr = 0, n_lm = 0, x_floats = 0, out_floats = 0, res_floats = 0;
   int pre_units = 0, pre_off = 0, n_stages = 0;
   int32_t s_qkv = 0, s_part = 0;  // per-sequence strides of qkv and part (words)
   int flag_stride = 0;
+  int x_cap = 0, pre_cap = -1;     // mkd_set_lds_limits
+  bool plain_launch = false;       // mkd_set_launch_mode
   hipEvent_t done = nullptr;
   hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
   bool launched = false, timed = false;
@@ -68,6 +86,77 @@ struct mkd_model {
   uint64_t* trace = nullptr;
   size_t trace_cap = 0;
 };
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+constexpr size_t kZeroBytes = 4096;
+constexpr size_t kCtrlWords = 16;   // host control block: int32 words the caller provides
+
+size_t align_ws(size_t n) { return (n + kWsAlign - 1) & ~(kWsAlign - 1); }
+int32_t round16i(int64_t n) { return (int32_t)((n + 15) / 16 * 16); }
+
+// the tables init writes: pointer table, RoPE table, status words, zero page
+void ws_fixed(const mkd_config* c, int32_t max_seq, WsLayout* L) {
+  const size_t n_ptr = W_GLOBAL + (size_t)c->n_layers * layer_slots(c);
+  L->wtab = 0;
+  L->rope = align_ws(L->wtab + n_ptr * 8);
+  L->status = align_ws(L->rope + (size_t)max_seq * c->head_dim * 4);   // cos and sin, hd/2 each
+  L->zero = align_ws(L->status + S_WORDS * 4);
+  L->fixed = align_ws(L->zero + kZeroBytes);
+}
+
+// The schedule and the tagged activation block of one schedule tensor: one
+// completion flag per instruction of each stage; h, aout, hmid, act and lm
+// interleave the sequences (element r of sequence b at r * batch + b); qkv
+// and part hold one block per sequence, 128-byte aligned.
+void ws_schedule(const mkd_config* c, const int32_t* words, size_t n, WsLayout* L) {
+  const int n_wg = words[H_NWG], n_chunks = words[H_NCHUNKS], batch = words[H_BATCH];
+  const int n_st = words[H_NSTAGES];
+  int flag_stride = kFlagAlign;
+  std::vector<int> per(n_st, 0);
+  const int32_t* body = words + kWords + n_wg;
+  for (int w = 0; w < n_wg; ++w)
+    for (int j = 0; j < words[kWords + w]; ++j) {
+      const int32_t* ins = body + ((size_t)w * words[H_MAXINSTR] + j) * kWords;
+      per[ins[I_STAGE]] = std::max(per[ins[I_STAGE]], ins[I_INDEX] + 1);
+    }
+  for (int v : per) flag_stride = std::max(flag_stride, (v + kFlagAlign - 1) / kFlagAlign * kFlagAlign);
+  const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
+  const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  L->s_qkv = round16i(qd + 2 * kvd);
+  L->s_part = round16i((int64_t)c->n_q_heads * n_chunks * (c->head_dim + 2));
+  const size_t sz[9] = {round16((size_t)c->d_model * batch), (size_t)batch * L->s_qkv, (size_t)batch * L->s_part,
+                        round16((size_t)qd * batch), round16((size_t)c->d_model * batch),
+                        round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1) * batch),
+                        16, round16(2 * (size_t)n_lm * batch),
+                        round16((size_t)n_st * flag_stride / 2)};
+  L->ll_words = 0;
+  for (int i = 0; i < 9; ++i) {
+    L->sz[i] = sz[i];
+    // the flags start on a 256-byte boundary, as do their per-stage arrays
+    if (i == 7) L->sz[i] += (32 - (L->ll_words + sz[i]) % 32) % 32;
+    L->ll_words += L->sz[i];
+  }
+  L->flag_stride = flag_stride;
+  L->sched_words = n;
+  L->sched = L->fixed;
+  L->ll = align_ws(L->sched + n * 4);
+  L->total = align_ws(L->ll + L->ll_words * 8);
+}
+
+// split-KV chunks when the caller leaves the choice to the library
+int default_chunks(const mkd_config* c, int n_wg, int n_positions) {
+  // one chunk (one attention instruction per q head) up to 512 KiB of K and V
+  // per head, else one chunk per workgroup and kv head (at most 64); measured
+  // best on the 1B and 3B shapes at KV 1024-16384
+  const double head_bytes = (double)n_positions * c->head_dim * 4.0;  // K and V rows
+  int cap = n_wg / c->n_kv_heads;
+  cap = cap < 1 ? 1 : (cap > 64 ? 64 : cap);
+  return head_bytes <= 512.0 * 1024 ? 1 : cap;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -151,13 +240,63 @@ int mkd_schedule_validate(const mkd_config* cfg, const int32_t* words, size_t n_
   return MKD_OK;
 }
 
+int mkd_default_chunks(const mkd_config* cfg, int32_t n_wg, int32_t n_positions, int32_t* n_chunks) {
+  const char* why = "";
+  if (!cfg || !n_chunks) return fail(MKD_E_INVALID, "null argument");
+  if (config_check(cfg, &why)) return fail(MKD_E_INVALID, why);
+  if (n_wg < 1 || n_positions < 1) return fail(MKD_E_INVALID, "n_wg and n_positions must be >= 1");
+  *n_chunks = default_chunks(cfg, n_wg, n_positions);
+  return MKD_OK;
+}
+
+int mkd_workspace_bytes(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch, int32_t max_seq,
+                        size_t* bytes_out) {
+  const char* why = "";
+  if (!cfg || !bytes_out) return fail(MKD_E_INVALID, "null argument");
+  if (config_check(cfg, &why)) return fail(MKD_E_INVALID, why);
+  if (max_seq < 1 || n_wg < 1) return fail(MKD_E_INVALID, "max_seq and n_wg must be >= 1");
+  if (n_chunks == 0) n_chunks = default_chunks(cfg, n_wg, max_seq);
+  size_t n = 0;
+  if (schedule_build(cfg, n_wg, n_chunks, batch, nullptr, 0, &n, &why)) return fail(MKD_E_INVALID, why);
+  std::vector<int32_t> w(n);
+  if (schedule_build(cfg, n_wg, n_chunks, batch, w.data(), n, &n, &why)) return fail(MKD_E_INVALID, why);
+  WsLayout L;
+  ws_fixed(cfg, max_seq, &L);
+  ws_schedule(cfg, w.data(), n, &L);
+  *bytes_out = L.total;
+  return MKD_OK;
+}
+
+int mkd_workspace_layout(const mkd_config* cfg, int32_t n_wg, int32_t n_chunks, int32_t batch, int32_t max_seq,
+                         size_t* offsets_out) {
+  size_t total = 0;
+  int rc = mkd_workspace_bytes(cfg, n_wg, n_chunks, batch, max_seq, &total);
+  if (rc) return rc;
+  if (!offsets_out) return fail(MKD_E_INVALID, "null offsets_out");
+  const char* why = "";
+  if (n_chunks == 0) n_chunks = default_chunks(cfg, n_wg, max_seq);
+  size_t n = 0;
+  schedule_build(cfg, n_wg, n_chunks, batch, nullptr, 0, &n, &why);
+  std::vector<int32_t> w(n);
+  schedule_build(cfg, n_wg, n_chunks, batch, w.data(), n, &n, &why);
+  WsLayout L;
+  ws_fixed(cfg, max_seq, &L);
+  ws_schedule(cfg, w.data(), n, &L);
+  const size_t v[8] = {L.wtab, L.rope, L.status, L.zero, L.sched, L.ll, L.ll + (L.ll_words - L.sz[8]) * 8, L.total};
+  for (int i = 0; i < 8; ++i) offsets_out[i] = v[i];
+  return MKD_OK;
+}
+
 int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
-             int32_t max_seq, int32_t device, mkd_model** out) {
-  return mkd_init_batch(cfg, weights, n_weights, kv_cache, max_seq, 1, device, out);
+             int32_t max_seq, void* workspace, size_t workspace_bytes, int32_t* host_control, int32_t device,
+             mkd_model** out) {
+  return mkd_init_batch(cfg, weights, n_weights, kv_cache, max_seq, 1, workspace, workspace_bytes, host_control,
+                        device, out);
 }
 
 int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
-                   int32_t max_seq, int32_t batch, int32_t device, mkd_model** out) {
+                   int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes, int32_t* host_control,
+                   int32_t device, mkd_model** out) {
   if (!out) return fail(MKD_E_INVALID, "null out");
   *out = nullptr;
   if (batch < 1 || batch > kMaxBatch) return fail(MKD_E_INVALID, "batch must be in [1, 8]");
@@ -179,6 +318,15 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   if (!kv_cache || ((uintptr_t)kv_cache & 15)) return fail(MKD_E_INVALID, "kv_cache null or misaligned");
   const size_t head_bytes = (size_t)max_seq * cfg->head_dim * 2;
   if (head_bytes > 0x7fffffffull) return fail(MKD_E_INVALID, "max_seq * head_dim too large");
+  WsLayout L;
+  ws_fixed(cfg, max_seq, &L);
+  if (!workspace || ((uintptr_t)workspace & (kWsAlign - 1)))
+    return fail(MKD_E_INVALID, "workspace null or not 256-byte aligned");
+  if (workspace_bytes < L.fixed)
+    return fail(MKD_E_INVALID, "workspace of " + std::to_string(workspace_bytes) + " bytes is smaller than the " +
+                                   std::to_string(L.fixed) + " its tables need (mkd_workspace_bytes sizes it)");
+  if (!host_control || ((uintptr_t)host_control & 63))
+    return fail(MKD_E_INVALID, "host_control null or not 64-byte aligned");
 
   hipError_t e = hipSetDevice(device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
@@ -190,6 +338,20 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   int coop = 0;
   hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device);
   if (!coop) return fail(MKD_E_UNSUPPORTED, "device lacks cooperative launch");
+  // the borrowed memory must be what the kernel can reach: device memory of
+  // this device, and pinned (device-mapped) host memory for the control block
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, workspace) != hipSuccess || at.type != hipMemoryTypeDevice ||
+      at.device != device) {
+    (void)hipGetLastError();
+    return fail(MKD_E_INVALID, "workspace is not device memory of device " + std::to_string(device));
+  }
+  hipPointerAttribute_t hc{};
+  if (hipPointerGetAttributes(&hc, host_control) != hipSuccess || hc.type != hipMemoryTypeHost ||
+      !hc.devicePointer) {
+    (void)hipGetLastError();
+    return fail(MKD_E_INVALID, "host_control is not pinned host memory mapped for the device");
+  }
 
   mkd_model* m = new mkd_model();
   m->cfg = *cfg;
@@ -198,6 +360,15 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   m->n_cu = prop.multiProcessorCount;
   m->max_seq = max_seq;
   m->kv = (uint16_t*)kv_cache;
+  m->ws = (char*)workspace;
+  m->ws_bytes = workspace_bytes;
+  m->lay = L;
+  m->d_wtab = (uint64_t*)(m->ws + L.wtab);
+  m->d_rope = (float*)(m->ws + L.rope);
+  m->d_status = (int32_t*)(m->ws + L.status);
+  m->d_zero = m->ws + L.zero;
+  m->h_ctrl = host_control;
+  m->d_stop = (const int32_t*)hc.devicePointer;
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
     m->clock_hz = (double)khz * 1e3;
@@ -227,14 +398,8 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
     mkd_destroy(m);
     return fail(code, msg);
   };
-  if ((e = hipMalloc(&m->d_wtab, m->wptr.size() * 8)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc wtab");
-  if ((e = hipMalloc(&m->d_rope, rope.size() * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc rope");
-  if ((e = hipMalloc(&m->d_status, S_WORDS * 4)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc status");
-  if ((e = hipMalloc(&m->d_zero, 4096)) != hipSuccess) return cleanup(MKD_E_HIP, "hipMalloc zero");
-  if ((e = hipMemset(m->d_zero, 0, 4096)) != hipSuccess) return cleanup(MKD_E_HIP, "clear zero");
-  if ((e = hipHostMalloc(&m->h_stop, 64, hipHostMallocDefault)) != hipSuccess)
-    return cleanup(MKD_E_HIP, "hipHostMalloc stop word");
-  memset(m->h_stop, 0, 64);
+  for (size_t i = 0; i < kCtrlWords; ++i) __atomic_store_n(host_control + i, 0, __ATOMIC_SEQ_CST);
+  if ((e = hipMemset(m->d_zero, 0, kZeroBytes)) != hipSuccess) return cleanup(MKD_E_HIP, "clear zero page");
   if ((e = hipMemcpy(m->d_wtab, m->wptr.data(), m->wptr.size() * 8, hipMemcpyHostToDevice)) != hipSuccess)
     return cleanup(MKD_E_HIP, "upload wtab");
   if ((e = hipMemcpy(m->d_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
@@ -293,23 +458,24 @@ static int res_floats_for(const mkd_config* c, int n_wg, int n_chunks, int batch
   return ((best + 3) & ~3) * batch;
 }
 
+// Limits a caller may put on the LDS plan (mkd_set_lds_limits): the batched
+// input area in floats (0 = none) and the staged gate/up units per wavefront
+// (-1 = none).  They only ever shrink what the plan would use.
+struct LdsCaps {
+  int x_cap = 0, pre_cap = -1;
+};
+
 // Dense gate/up weights staged in LDS ahead of the instruction: as many
-// 1 KiB units per wavefront as the LDS left over holds, up to kPreMax
-// (MKD_PRE_UNITS overrides, within the same bounds).  They are loaded while
-// the workgroup waits out the attention phase, when its own load queue is
-// otherwise empty.
-static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max) {
+// 1 KiB units per wavefront as the LDS left over holds, up to kPreMax (and
+// the caller's cap).  They are loaded while the workgroup waits out the
+// attention phase, when its own load queue is otherwise empty.
+static int pre_units_for(const mkd_config* c, size_t lds_used, int lds_max, const LdsCaps& caps) {
   if (c->n_experts > 0 || lds_max <= 0 || lds_used >= (size_t)lds_max) return 0;
   int n = (int)(((size_t)lds_max - lds_used) / ((size_t)kWaves * 1024));
   if (n > kPreMax) n = kPreMax;
-  if (const char* e = getenv("MKD_PRE_UNITS")) {
-    const int want = atoi(e);
-    if (want >= 0 && want < n) n = want;
-  }
+  if (caps.pre_cap >= 0 && caps.pre_cap < n) n = caps.pre_cap;
   return n;
 }
-
-static int32_t round16i(int64_t n) { return (int32_t)((n + 15) / 16 * 16); }
 
 // LDS floats of one input vector of n elements per sequence: one sequence
 // reads x in 512-wide segments; with several sequences, interleaved, every
@@ -346,13 +512,14 @@ constexpr size_t kLdsSlack = 256;  // static LDS of the kernel and a margin
 // whole 512-element segments per sequence; the down projection then runs in
 // passes over K.  The other inputs (normalised as a whole) are never split:
 // if even they do not fit, the area is left as is and the LDS check fails.
-// MKD_BATCH_X_FLOATS caps the area further (within the same bounds), so that
-// the passes can be exercised on small models.
-static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int batch, int lds_max) {
+// The caller's cap shrinks the area further (within the same bounds), so
+// that the passes can be exercised on small models.
+static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int batch, int lds_max,
+                  const LdsCaps& caps) {
   if (batch == 1) return;
-  if (const char* e = getenv("MKD_BATCH_X_FLOATS")) {
+  if (caps.x_cap > 0) {
     const int seg = 64 * (8 * batch + 4);   // one 512-element segment of every sequence, padded
-    const int cap = atoi(e) / seg * seg;
+    const int cap = caps.x_cap / seg * seg;
     if (cap > 0 && cap < p.x_floats && cap >= x_floats_for(c, n_chunks, n_lm, batch, false)) {
       p.x_floats = cap;
       return;
@@ -378,10 +545,10 @@ static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int b
 // the input area past the two inputs that are live while the units are
 // (the O-projection's, read while they load, and gate/up's own); the down
 // projection's longer input reuses that space after gate/up has read them.
-static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max) {
+static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max, const LdsCaps& caps) {
   p.pre_off = 0;
   if (batch == 1) {
-    p.pre_units = pre_units_for(c, lds_bytes(p), lds_max);
+    p.pre_units = pre_units_for(c, lds_bytes(p), lds_max, caps);
     return;
   }
   p.pre_units = 0;
@@ -394,10 +561,7 @@ static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max) {
   if (off >= p.x_floats) return;
   int n = (p.x_floats - off) / (kWaves * 256);   // 1 KiB units per wavefront
   n = std::min(n, kPreMax);
-  if (const char* e = getenv("MKD_PRE_UNITS")) {
-    const int want = atoi(e);
-    if (want >= 0 && want < n) n = want;
-  }
+  if (caps.pre_cap >= 0 && caps.pre_cap < n) n = caps.pre_cap;
   if (n < 4) return;   // the batched streamer stages whole groups of 4 rows
   p.pre_off = off;
   p.pre_units = n;
@@ -406,15 +570,16 @@ static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max) {
 // The per-workgroup LDS areas of a schedule (n_wg workgroups, n_chunks
 // split-KV chunks, batch sequences) on a device with lds_max bytes per
 // workgroup (0: unknown, no fitting).
-static KParams lds_plan(const mkd_config* c, int n_wg, int n_chunks, int batch, int lds_max) {
+static KParams lds_plan(const mkd_config* c, int n_wg, int n_chunks, int batch, int lds_max,
+                        const LdsCaps& caps = LdsCaps()) {
   const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
   KParams p{};
   p.x_floats = x_floats_for(c, n_chunks, n_lm, batch);
   p.out_floats = out_floats_for(c, n_wg, n_chunks, batch);
   p.res_floats = res_floats_for(c, n_wg, n_chunks, batch);
   p.d = c->d_model;
-  fit_x(p, c, n_chunks, n_lm, batch, lds_max);
-  set_pre(p, c, batch, lds_max);
+  fit_x(p, c, n_chunks, n_lm, batch, lds_max, caps);
+  set_pre(p, c, batch, lds_max, caps);
   return p;
 }
 
@@ -461,8 +626,10 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   const int n_lm = c->vocab < n_wg ? c->vocab : n_wg;
   int lds_max = 0;
   hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, m->device);
-  const KParams p = lds_plan(c, n_wg, n_chunks, batch, lds_max);
-  const int out_floats = p.out_floats, res_floats = p.res_floats;
+  LdsCaps caps;
+  caps.x_cap = m->x_cap;
+  caps.pre_cap = m->pre_cap;
+  const KParams p = lds_plan(c, n_wg, n_chunks, batch, lds_max, caps);
   const size_t lds = lds_bytes(p);
   if (lds_max > 0 && lds > (size_t)lds_max)
     return fail(MKD_E_UNSUPPORTED, "schedule needs " + std::to_string(lds) + " bytes of LDS per workgroup, device has " +
@@ -473,69 +640,37 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   if (n_wg > mx)
     return fail(MKD_E_COOPERATIVE, "n_wg " + std::to_string(n_wg) + " exceeds the " +
                                        std::to_string(mx) + " workgroups that can be co-resident");
+  WsLayout L = m->lay;
+  ws_schedule(c, words, n, &L);
+  if (L.total > m->ws_bytes)
+    return fail(MKD_E_INVALID, "this schedule needs a workspace of " + std::to_string(L.total) + " bytes, the handle has " +
+                                   std::to_string(m->ws_bytes) + " (mkd_workspace_bytes sizes it)");
   hipError_t e = hipSetDevice(m->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
   if (m->launched) hipEventSynchronize(m->done);
-  if (n > m->sched_cap) {
-    if (m->d_sched) hipFree(m->d_sched);
-    m->d_sched = nullptr;
-    m->sched_cap = 0;
-    if ((e = hipMalloc(&m->d_sched, n * 4)) != hipSuccess) return hip_fail(e, "hipMalloc schedule");
-    m->sched_cap = n;
-  }
+  m->lay = L;
+  m->d_sched = (int32_t*)(m->ws + L.sched);
   if ((e = hipMemcpy(m->d_sched, words, n * 4, hipMemcpyHostToDevice)) != hipSuccess)
     return hip_fail(e, "upload schedule");
   m->sched_words = n;
-  // completion flags: one word per instruction of each stage
-  int flag_stride = kFlagAlign;
-  {
-    const int n_st = words[H_NSTAGES];
-    std::vector<int> per(n_st, 0);
-    const int32_t* body = words + kWords + n_wg;
-    for (int w = 0; w < n_wg; ++w)
-      for (int j = 0; j < words[kWords + w]; ++j) {
-        const int32_t* ins = body + ((size_t)w * words[H_MAXINSTR] + j) * kWords;
-        per[ins[I_STAGE]] = std::max(per[ins[I_STAGE]], ins[I_INDEX] + 1);
-      }
-    for (int v : per) flag_stride = std::max(flag_stride, (v + kFlagAlign - 1) / kFlagAlign * kFlagAlign);
-  }
-  // tagged activation buffers, one allocation (cleared before each launch):
-  // h, aout, hmid, act and lm interleave the sequences (element r of sequence
-  // b at r * batch + b); qkv and part hold one block per sequence, 128-byte
-  // aligned
-  const int qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
-  const int32_t s_qkv = round16i(qd + 2 * kvd),
-                s_part = round16i((int64_t)c->n_q_heads * n_chunks * (c->head_dim + 2));
-  const size_t sz[9] = {round16((size_t)c->d_model * batch), (size_t)batch * s_qkv, (size_t)batch * s_part,
-                        round16((size_t)qd * batch), round16((size_t)c->d_model * batch),
-                        round16((size_t)c->d_ff * (c->top_k ? c->top_k : 1) * batch),
-                        16, round16(2 * (size_t)n_lm * batch),
-                        round16((size_t)words[H_NSTAGES] * flag_stride / 2)};
-  size_t total = 0;
-  for (size_t s : sz) total += s;
-  if (total > m->ll_cap) {
-    if (m->d_ll) hipFree(m->d_ll);
-    m->d_ll = nullptr;
-    m->ll_cap = 0;
-    if ((e = hipMalloc(&m->d_ll, total * 8)) != hipSuccess) return hip_fail(e, "hipMalloc activations");
-    m->ll_cap = total;
-  }
-  m->ll_words = total;
+  // the tagged activation block, cleared before each launch
+  m->d_ll = (uint64_t*)(m->ws + L.ll);
+  m->ll_words = L.ll_words;
   uint64_t* q = m->d_ll;
   uint64_t** dst[9] = {&m->h, &m->qkv, &m->part, &m->aout, &m->hmid, &m->act, &m->route, &m->lm, &m->flags};
-  for (int i = 0; i < 9; ++i) { *dst[i] = q; q += sz[i]; }
+  for (int i = 0; i < 9; ++i) { *dst[i] = q; q += L.sz[i]; }
   m->n_stages = words[H_NSTAGES];
-  m->flag_stride = flag_stride;
+  m->flag_stride = L.flag_stride;
   m->n_wg = n_wg;
   m->n_chunks = n_chunks;
   m->max_instr = words[H_MAXINSTR];
   m->n_lm = n_lm;
   m->x_floats = p.x_floats;
-  m->out_floats = out_floats;
-  m->res_floats = res_floats;
+  m->out_floats = p.out_floats;
+  m->res_floats = p.res_floats;
   m->pre_units = p.pre_units;
   m->pre_off = p.pre_off;
-  m->s_qkv = s_qkv; m->s_part = s_part;
+  m->s_qkv = L.s_qkv; m->s_part = L.s_part;
   return MKD_OK;
 }
 
@@ -550,15 +685,7 @@ int mkd_build_schedule(mkd_model* m, int32_t n_wg, int32_t n_chunks, int32_t* ho
                        size_t capacity, size_t* n_words) {
   if (!m) return fail(MKD_E_INVALID, "null model");
   if (n_wg == 0) n_wg = m->n_cu;
-  if (n_chunks == 0) {
-    // one chunk (one attention instruction per q head) up to 512 KiB of K and
-    // V per head at max_seq, else one chunk per workgroup and kv head (at
-    // most 64); measured best on the 1B and 3B shapes at KV 1024-16384
-    const double head_bytes = (double)m->max_seq * m->cfg.head_dim * 4.0;  // K and V rows
-    int cap = n_wg / m->cfg.n_kv_heads;
-    cap = cap < 1 ? 1 : (cap > 64 ? 64 : cap);
-    n_chunks = head_bytes <= 512.0 * 1024 ? 1 : cap;
-  }
+  if (n_chunks == 0) n_chunks = default_chunks(&m->cfg, n_wg, m->max_seq);
   size_t n = 0;
   int rc = mkd_schedule_build_batch(&m->cfg, n_wg, n_chunks, m->batch, nullptr, 0, &n);
   if (rc) return rc;
@@ -591,6 +718,16 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   if ((int64_t)n_steps * (c->n_layers + 1) >= 0xffffffffll) return fail(MKD_E_INVALID, "n_steps too large");
   hipError_t e = hipSetDevice(m->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  if (m->launched) {
+    // the reset kernel of a new launch would clear the flags and activations
+    // a running one still uses (on another stream it would not wait for it)
+    const hipError_t q = hipEventQuery(m->done);
+    if (q == hipErrorNotReady) return fail(MKD_E_INVALID, "the previous launch is still running: mkd_wait first");
+    if (q != hipSuccess) return hip_fail(q, "previous launch");
+    m->launched = false;   // finished; its status is superseded by this launch
+  }
+  // a stop requested while no launch was running must not end this one
+  __atomic_store_n(m->h_ctrl, 0, __ATOMIC_SEQ_CST);
   KParams p{};
   p.sched = m->d_sched;
   p.wtab = m->d_wtab;
@@ -606,7 +743,7 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   p.tokens_out = tokens_out_dev;
   p.logits_out = logits_out_dev;
   p.status = m->d_status;
-  p.stop = m->h_stop;
+  p.stop = m->d_stop;
   p.trace = m->trace;
   p.watchdog_ticks = m->watchdog_ticks;
   p.n_wg = m->n_wg; p.max_instr = m->max_instr; p.n_chunks = m->n_chunks; p.n_lm_tiles = m->n_lm;
@@ -629,7 +766,7 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   p.pre_off = m->pre_off;
   p.eps = c->rms_eps;
   const char* why = "";
-  const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, &why);
+  const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, !m->plain_launch, &why);
   if (rc) return fail(rc, why);
   m->timed = true;
   if ((e = hipEventRecord(m->done, (hipStream_t)stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -669,7 +806,7 @@ int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out) {
   hipError_t e = hipMemcpy(st, m->d_status, sizeof(st), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "read status");
   m->launched = false;
-  __atomic_store_n(m->h_stop, 0, __ATOMIC_SEQ_CST);
+  __atomic_store_n(m->h_ctrl, 0, __ATOMIC_SEQ_CST);
   if (out) *out = mkd_status{st[S_CODE], st[S_WG], st[S_INSTR], st[S_TOKEN]};
   if (st[S_CODE] != MKD_OK) {
     return fail(st[S_CODE], "device reported error " + std::to_string(st[S_CODE]) + " at workgroup " +
@@ -681,7 +818,24 @@ int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out) {
 
 int mkd_abort(mkd_model* m) {
   if (!m) return fail(MKD_E_INVALID, "null model");
-  __atomic_store_n(m->h_stop, 1, __ATOMIC_SEQ_CST);
+  // only a launch that is in flight can be stopped; the next launch clears
+  // the word again before it starts
+  if (m->launched) __atomic_store_n(m->h_ctrl, 1, __ATOMIC_SEQ_CST);
+  return MKD_OK;
+}
+
+int mkd_set_lds_limits(mkd_model* m, int32_t max_input_floats, int32_t max_staged_units) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (max_input_floats < 0 || max_staged_units < -1) return fail(MKD_E_INVALID, "limits out of range");
+  m->x_cap = max_input_floats;
+  m->pre_cap = max_staged_units;
+  return MKD_OK;
+}
+
+int mkd_set_launch_mode(mkd_model* m, int32_t cooperative) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (cooperative != 0 && cooperative != 1) return fail(MKD_E_INVALID, "cooperative must be 0 or 1");
+  m->plain_launch = cooperative == 0;
   return MKD_OK;
 }
 
@@ -721,13 +875,6 @@ void mkd_destroy(mkd_model* m) {
   if (m->done) hipEventDestroy(m->done);
   if (m->k0) hipEventDestroy(m->k0);
   if (m->k1) hipEventDestroy(m->k1);
-  if (m->d_wtab) hipFree(m->d_wtab);
-  if (m->d_rope) hipFree(m->d_rope);
-  if (m->d_status) hipFree(m->d_status);
-  if (m->d_zero) hipFree(m->d_zero);
-  if (m->h_stop) hipHostFree(m->h_stop);
-  if (m->d_ll) hipFree(m->d_ll);
-  if (m->d_sched) hipFree(m->d_sched);
   delete m;
 }
 

@@ -1,6 +1,8 @@
-// Persistent decode megakernel for gfx950 (MI355X): one sequence (dense or
-// MoE model) or 2-8 sequences decoded together (dense), each its own
-// instantiation of the same persistent loop.
+// Device code of the persistent decode megakernel for gfx950 (MI355X): one
+// sequence (dense or MoE model) or 2-8 sequences decoded together (dense),
+// each its own instantiation of the same persistent loop (one translation
+// unit per kernel: mkd_kernel_dense.hip, mkd_kernel_moe.hip,
+// mkd_kernel_batch.hip; the launch code is in mkd_launch.hip).
 //
 // One cooperative launch; one 512-thread workgroup per compute unit; every
 // workgroup walks its slice of a host-built instruction tensor for every
@@ -27,6 +29,8 @@
 // B200 bandwidth" and "L2 prefetching overlapped with prior instructions";
 // Hyperkernel teardown: next-layer tiles load while the current layer runs).
 // Wavefront reductions use DPP row permutes plus readlane.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdlib.h>
@@ -71,7 +75,6 @@ __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) { *(GLOBAL uint6
 
 constexpr int RING = 8;       // 16-byte weight loads in flight per lane (GEMV)
 constexpr int ARING = 4;      // K/V position steps in flight per lane (attention)
-constexpr int kRed = 256;     // LDS floats reserved for reductions
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kSC1 = 16;                     // cache-policy bit: device-coherent access
 constexpr int kNT = 2;                       // cache-policy bit: non-temporal (streamed once)
@@ -2093,7 +2096,7 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
 
 // ---------------------------------------------------------------- the kernel
 
-__shared__ int s_flags[8];
+static __shared__ int s_flags[8];
 
 // The persistent loop.  Three kernels instantiate it: dense models with one
 // sequence (batch size the constant 1), MoE models with one sequence, and
@@ -2189,96 +2192,6 @@ __device__ __forceinline__ void megakernel_body() {
       }
     }
   }
-}
-
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel(KParams params) {
-  (void)params;
-  megakernel_body<K_DENSE>();
-}
-
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel_moe(KParams params) {
-  (void)params;
-  megakernel_body<K_MOE>();
-}
-
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mkd_megakernel_batch(KParams params) {
-  (void)params;
-  megakernel_body<K_BATCH>();
-}
-
-extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) ll[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < S_WORDS) {
-    const int k = threadIdx.x;
-    status[k] = (k == S_WG || k == S_INSTR || k == S_TOKEN) ? -1 : 0;
-  }
-}
-
-// ---------------------------------------------------------------- host-side launch
-
-size_t lds_bytes(const KParams& p) {
-  return ((size_t)p.x_floats + (size_t)p.res_floats + (size_t)p.out_floats + kRed) * sizeof(float) +
-         (p.pre_off ? 0 : (size_t)p.pre_units * kWaves * 1024);
-}
-
-// the persistent kernel for `batch` sequences of a dense or MoE model
-static const void* kernel_for(int batch, bool moe) {
-  return batch > 1 ? (const void*)mkd_megakernel_batch
-                   : (moe ? (const void*)mkd_megakernel_moe : (const void*)mkd_megakernel);
-}
-
-int max_coop_blocks(int device, size_t lds, int batch, bool moe, int* out) {
-  if (hipSetDevice(device) != hipSuccess) return MKD_E_HIP;
-  const void* k = kernel_for(batch, moe);
-  if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return MKD_E_HIP;
-  int per_cu = 0, n_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, lds) != hipSuccess)
-    return MKD_E_HIP;
-  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-    return MKD_E_HIP;
-  *out = per_cu * n_cu;
-  return MKD_OK;
-}
-
-int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why) {
-  hipStream_t s = (hipStream_t)stream;
-  const size_t lds = lds_bytes(p);
-  int blocks = (int)((ll_words + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(mkd_reset, dim3(blocks), dim3(256), 0, s, p.h, ll_words, p.status);
-  if (hipGetLastError() != hipSuccess) { *why = "reset kernel launch failed"; return MKD_E_HIP; }
-  const void* k = kernel_for(p.B, p.E > 0);
-  if (lds > 64 * 1024 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-    *why = "cannot raise the kernel's LDS limit";
-    return MKD_E_HIP;
-  }
-  KParams pc = p;
-  void* args[] = {&pc};
-  if (ev0 && hipEventRecord((hipEvent_t)ev0, s) != hipSuccess) { *why = "hipEventRecord"; return MKD_E_HIP; }
-  // MKD_LAUNCH=plain dispatches the same grid without the cooperative flag.  The
-  // grid was already checked to fit co-resident (max_coop_blocks), so on an idle
-  // device every workgroup is resident at once either way; the switch exists for
-  // profilers that cannot finish their output after a cooperative dispatch.
-  static const bool plain = [] {
-    const char* v = getenv("MKD_LAUNCH");
-    return v && strcmp(v, "plain") == 0;
-  }();
-  const hipError_t e =
-      plain ? hipLaunchKernel(k, dim3(p.n_wg), dim3(kThreads), args, (unsigned)lds, s)
-            : hipLaunchCooperativeKernel(k, dim3(p.n_wg), dim3(kThreads), args, (unsigned)lds, s);
-  if (e == hipErrorCooperativeLaunchTooLarge) {
-    *why = "grid does not fit co-resident on the device";
-    return MKD_E_COOPERATIVE;
-  }
-  if (e != hipSuccess) {
-    *why = hipGetErrorString(e);
-    return MKD_E_HIP;
-  }
-  if (ev1 && hipEventRecord((hipEvent_t)ev1, s) != hipSuccess) { *why = "hipEventRecord"; return MKD_E_HIP; }
-  return MKD_OK;
 }
 
 }  // namespace mkd

@@ -56,6 +56,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kPreMax = 16;   // cap on pre_units
 constexpr int kFlagAlign = 64;   // per-stage flag arrays start on 256-byte boundaries
 constexpr int kTraceWords = 4;   // per instruction: start, inputs ready, end, unused
+constexpr int kRed = 256;        // LDS floats reserved for reductions
 
 // weight pointer table layout: global slots, then per-layer slots
 constexpr int W_EMBED = 0, W_FINAL_NORM = 1, W_LM_HEAD = 2, W_GLOBAL = 3;
@@ -87,7 +88,7 @@ struct KParams {
   int32_t* tokens_out;       // [n_steps]
   float* logits_out;         // [n_steps][V] or null
   int32_t* status;           // [S_WORDS]
-  const int32_t* stop;       // pinned host word
+  const int32_t* stop;       // stop word: device address of the caller's pinned host control block
   uint64_t* trace;           // or null
   uint64_t watchdog_ticks;
   int32_t n_wg, max_instr, n_chunks, n_lm_tiles, n_stages, flag_stride;
@@ -115,11 +116,17 @@ struct KParams {
 };
 
 size_t lds_bytes(const KParams& p);
-// launch the reset kernel and the cooperative megakernel on `stream`
-// ev0/ev1 (may be null) are recorded around the cooperative kernel alone
-int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, const char** why);
+// launch the reset kernel and the megakernel (cooperatively, or as a plain
+// dispatch of the same grid) on `stream`; ev0/ev1 (may be null) are recorded
+// around the megakernel alone
+int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1, bool cooperative,
+           const char** why);
 // co-resident workgroups of the persistent kernel for `batch` sequences of a
 // dense or MoE model
 int max_coop_blocks(int device, size_t lds, int batch, bool moe, int* out);
+// host-side handles of the persistent kernels (one translation unit each)
+const void* kernel_dense();
+const void* kernel_moe();
+const void* kernel_batch();
 
 }  // namespace mkd

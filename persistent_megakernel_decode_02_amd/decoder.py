@@ -1,4 +1,5 @@
-"""Keeps the torch tensors a libmkd handle borrows alive, and turns calls into
+"""Keeps the torch tensors a libmkd handle borrows alive (weights, KV cache,
+the device workspace and the pinned host control block), and turns calls into
 the C ABI's (argument marshalling only; all compute runs in the library)."""
 from __future__ import annotations
 
@@ -11,12 +12,18 @@ from . import capi
 
 class Decoder:
     """One model on one GPU: weights (bf16 device tensors in pointer order),
-    a bf16 KV cache tensor, and the library handle with a loaded schedule.
-    With ``batch`` > 1 the cache tensor holds every sequence's cache, one
-    after the other, and decoding goes through ``decode_batch``."""
+    a bf16 KV cache tensor, the library's workspace (a uint8 device tensor
+    sized by mkd_workspace_bytes for the launch shape), its pinned host
+    control block, and the library handle with a loaded schedule.  With
+    ``batch`` > 1 the cache tensor holds every sequence's cache, one after
+    the other, and decoding goes through ``decode_batch``.  ``cooperative``
+    False dispatches the same grid without the cooperative flag (profiling);
+    ``lds_limits`` = (max input floats, max staged units) is passed to
+    mkd_set_lds_limits before the schedule is built (tests)."""
 
     def __init__(self, cfg, weights: Sequence[torch.Tensor], kv_cache: torch.Tensor, max_seq: int,
-                 n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None, batch: int = 1):
+                 n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None, batch: int = 1,
+                 cooperative: bool = True, lds_limits=None):
         self.cfg = cfg
         self.ccfg = capi.make_config(cfg)
         self.weights = list(weights)
@@ -32,7 +39,19 @@ class Decoder:
             raise ValueError("kv cache must be contiguous bf16")
         if kv_cache.numel() * 2 != batch * capi.mkd_kv_cache_bytes(self.ccfg, max_seq):
             raise ValueError("kv cache size does not match max_seq and batch")
-        self.handle = capi.mkd_init_batch(self.ccfg, self.weights, kv_cache, max_seq, batch, self.device)
+        if n_wg == 0:
+            n_wg = torch.cuda.get_device_properties(self.device).multi_processor_count
+        if n_chunks == 0:
+            n_chunks = capi.mkd_default_chunks(self.ccfg, n_wg, max_seq)
+        nbytes = capi.mkd_workspace_bytes(self.ccfg, n_wg, n_chunks, batch, max_seq)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=kv_cache.device)
+        self.control = torch.zeros(capi.CONTROL_WORDS, dtype=torch.int32, pin_memory=True)
+        self.handle = capi.mkd_init_batch(self.ccfg, self.weights, kv_cache, max_seq, batch, self.workspace,
+                                          self.control, self.device)
+        if not cooperative:
+            capi.mkd_set_launch_mode(self.handle, False)
+        if lds_limits is not None:
+            capi.mkd_set_lds_limits(self.handle, *lds_limits)
         self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
 
     @property
@@ -48,6 +67,8 @@ class Decoder:
         return int(self.schedule[4])
 
     def rebuild(self, n_wg: int = 0, n_chunks: int = 0) -> None:
+        """Build and load another schedule; it must fit the workspace sized at
+        construction (the library checks)."""
         self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
 
     def launch(self, first_token: int, start_pos: int, n_steps: int, tokens_out: torch.Tensor,

@@ -1,8 +1,9 @@
 """Algorithmic HBM bytes of batch-1 decode and the bandwidth floor.
 
-At batch 1 every weight a step needs must cross HBM at least once, so bytes
-divided by bandwidth is a floor no kernel can beat (Hyperkernel teardown,
-"Where the numbers sit against the hardware").  Counted per step at position
+A batch-1 step reads each weight it uses at least once per step, so its
+algorithmic bytes over the peak bandwidth bound the step time from below (the
+weight-read floor of the Hyperkernel teardown, "Where the numbers sit against
+the hardware").  Counted per step at position
 p (p + 1 visible positions):
 
 * every weight the step reads: all dense matrices and norm gains, the full

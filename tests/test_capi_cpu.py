@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version():
-    assert capi.mkd_version() == 2
+    assert capi.mkd_version() == 3
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama1b", "llama3b", "mixtral"])
@@ -120,8 +120,86 @@ def test_init_batch_rejects_batch_out_of_range_and_moe():
                               ("tiny_moe", 2, capi.MKD_E_UNSUPPORTED)):
         c = capi.make_config(synth.PRESETS[name])
         with pytest.raises(capi.MkdError) as e:
-            capi.mkd_init_batch(c, [], None, 64, batch)
+            capi.mkd_init_batch(c, [], None, 64, batch, None, None)
         assert e.value.code == code
+
+
+def test_init_rejects_missing_or_small_workspace_before_any_device_call():
+    """Weights, cache, workspace and control block are checked on the host
+    first: a null, misaligned or too small workspace and a null control block
+    are MKD_E_INVALID (fake aligned addresses; nothing is dereferenced)."""
+    cfg = synth.PRESETS["tiny"]
+    c = capi.make_config(cfg)
+    lib = capi.load()
+    import ctypes
+    n = capi.mkd_weight_count(c)
+    ptrs = (ctypes.c_void_p * n)(*[0x10000 + 256 * i for i in range(n)])
+    h = ctypes.c_void_p()
+    need = capi.mkd_workspace_layout(c, 8, 1, 1, 64)
+    cases = [(0, 1 << 20, 0x40000), (0x20010, 1 << 20, 0x40000),       # null / misaligned workspace
+             (0x20000, need["zero"], 0x40000),                          # smaller than its tables
+             (0x20000, 1 << 20, 0), (0x20000, 1 << 20, 0x40010)]        # null / misaligned control
+    for ws, nbytes, ctrl in cases:
+        rc = lib.mkd_init(ctypes.byref(c), ptrs, n, 0x30000, 64, ws, nbytes, ctrl, 0, ctypes.byref(h))
+        assert rc == capi.MKD_E_INVALID, (ws, nbytes, ctrl, capi.mkd_last_error())
+        assert not h.value
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_moe", "llama1b", "llama3b", "mixtral"])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_workspace_layout(name, batch):
+    """The workspace regions: in order, 256-byte aligned, each as large as
+    what it holds -- the pointer table (one per weight slot), the RoPE cos and
+    sin table (max_seq x head_dim/2 each, fp32), 8 status words, a 4 KiB zero
+    page, the schedule tensor (as built for the same arguments) and the tagged
+    activation block, whose completion flags hold one word per instruction of
+    every stage -- and the total is mkd_workspace_bytes."""
+    cfg = synth.PRESETS[name]
+    if cfg.is_moe and batch > 1:
+        pytest.skip("batched decode is dense only")
+    c = capi.make_config(cfg)
+    max_seq = 1000
+    for n_wg, n_chunks in ((256, 1), (33, 4), (7, 2)):
+        L = capi.mkd_workspace_layout(c, n_wg, n_chunks, batch, max_seq)
+        offs = [L[k] for k in capi.WORKSPACE_REGIONS]
+        assert all(o % 256 == 0 for o in offs), L
+        assert offs == sorted(offs) and L["wtab"] == 0
+        assert L["total"] == capi.mkd_workspace_bytes(c, n_wg, n_chunks, batch, max_seq)
+        slots = 9 if not cfg.is_moe else 7 + 3 * cfg.n_experts
+        assert L["rope"] - L["wtab"] >= 8 * (3 + cfg.n_layers * slots)
+        assert L["status"] - L["rope"] >= 4 * max_seq * cfg.head_dim
+        assert L["zero"] - L["status"] >= 32 and L["schedule"] - L["zero"] >= 4096
+        words = capi.mkd_schedule_build_batch(c, n_wg, n_chunks, batch)
+        assert L["activations"] - L["schedule"] >= 4 * words.size
+        hdr, lists = S.parse(words)
+        n_stages = hdr[3]
+        per_stage = np.zeros(n_stages, dtype=np.int64)
+        for lst in lists:
+            for ins in lst:
+                per_stage[ins[2]] = max(per_stage[ins[2]], ins[3] + 1)
+        stride = int(max(64, ((per_stage.max() + 63) // 64) * 64))
+        assert L["total"] - L["flags"] >= 4 * n_stages * stride
+        # the activation words ahead of the flags: h, qkv, partials, attention
+        # output, mid residual, FFN activations, route, LM-head partials
+        qd, kvd, d = cfg.qd, cfg.kvd, cfg.d_model
+        n_lm = min(cfg.vocab, n_wg)
+        act = (d * batch + (qd + 2 * kvd) * batch + cfg.n_q_heads * n_chunks * (cfg.head_dim + 2) * batch
+               + qd * batch + d * batch + cfg.d_ff * max(1, cfg.top_k) * batch + 4 + 2 * n_lm * batch)
+        assert L["flags"] - L["activations"] >= 8 * act
+
+
+def test_default_chunks_rule():
+    """One chunk up to 512 KiB of K and V per kv head, else n_wg / n_kv_heads
+    chunks (1 to 64)."""
+    c1 = capi.make_config(synth.PRESETS["llama1b"])     # 256 bytes of K+V per position and head
+    assert capi.mkd_default_chunks(c1, 256, 2048) == 1
+    assert capi.mkd_default_chunks(c1, 256, 2049) == 32
+    assert capi.mkd_default_chunks(c1, 1024, 32768) == 64
+    assert capi.mkd_default_chunks(c1, 4, 32768) == 1   # fewer workgroups than kv heads: one chunk each
+    c3 = capi.make_config(synth.PRESETS["llama3b"])     # 512 bytes per position and head
+    assert capi.mkd_default_chunks(c3, 256, 1024) == 1 and capi.mkd_default_chunks(c3, 256, 1025) == 32
+    with pytest.raises(capi.MkdError):
+        capi.mkd_default_chunks(c1, 0, 100)
 
 
 LDS_MAX = 160 * 1024   # bytes of LDS per workgroup on gfx950

@@ -21,7 +21,7 @@ def _caches(cfg, max_seq, starts, device):
             for b, s in enumerate(starts)]
 
 
-def _run_batched(cfg, starts, N, n_wg, n_chunks, gain_std):
+def _run_batched(cfg, starts, N, n_wg, n_chunks, gain_std, lds_limits=None):
     B = len(starts)
     max_seq = max(starts) + N
     w_gpu = synth.gen_weights(cfg, device="cuda", gain_std=gain_std)
@@ -29,7 +29,7 @@ def _run_batched(cfg, starts, N, n_wg, n_chunks, gain_std):
     kv0 = kv_gpu.clone()
     firsts = synth.gen_tokens(B, cfg.vocab, stream=11)
     say(f"{cfg.name} B={B} starts={starts} steps={N} n_wg={n_wg} n_chunks={n_chunks}")
-    dec = Decoder(cfg, w_gpu, kv_gpu, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B)
+    dec = Decoder(cfg, w_gpu, kv_gpu, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B, lds_limits=lds_limits)
     toks, logits = dec.decode_batch(firsts, starts, N)
     toks2, logits2 = dec.decode_batch(firsts, starts, N)
     assert torch.equal(toks, toks2) and torch.equal(logits, logits2), "two identical launches differ"
@@ -64,15 +64,14 @@ def test_tiny_batched_kv_context(B, n_wg, n_chunks):
 
 
 @pytest.mark.parametrize("B,n_wg,n_chunks", [(3, 33, 2), (8, 256, 1)])
-def test_tiny_batched_down_projection_in_passes(B, n_wg, n_chunks, monkeypatch):
+def test_tiny_batched_down_projection_in_passes(B, n_wg, n_chunks):
     """The LDS input area capped to one 512-element segment of every sequence: the
     down projection (d_ff 768) then streams its rows in two passes over K,
     the second ragged, adding to the first pass's partial sums."""
     require_gpu()
-    monkeypatch.setenv("MKD_BATCH_X_FLOATS", str(64 * (8 * B + 4)))
     cfg = synth.PRESETS["tiny"]
     starts, N = STARTS[:B], 5
-    res = _run_batched(cfg, starts, N, n_wg, n_chunks, 0.1)
+    res = _run_batched(cfg, starts, N, n_wg, n_chunks, 0.1, lds_limits=(64 * (8 * B + 4), -1))
     _check_against_oracle(cfg, starts, N, res, 0.1)
 
 
@@ -101,17 +100,16 @@ def test_tiny_batched_random_launch_shapes(B, n_wg, n_chunks, starts):
 
 
 @pytest.mark.parametrize("B,n_wg", [(2, 7), (4, 256), (3, 33)])
-def test_tiny_batched_staged_gate_up_bit_exact(B, n_wg, monkeypatch):
+def test_tiny_batched_staged_gate_up_bit_exact(B, n_wg):
     """Gate/up weight rows staged in LDS during the attention phase are consumed in
     the order the streamer would load them, so the results are bit-identical to a
-    launch with no staging (MKD_PRE_UNITS=0). n_wg 7 stages 4 of a wavefront's 7
+    launch with no staging (staged units limited to 0). n_wg 7 stages 4 of a wavefront's 7
     steps (the rest streamed); n_wg 256 stages every step."""
     require_gpu()
     cfg = synth.PRESETS["tiny"]
     starts, N = STARTS[:B], 4
     staged = _run_batched(cfg, starts, N, n_wg, 1, 0.1)
-    monkeypatch.setenv("MKD_PRE_UNITS", "0")
-    plain = _run_batched(cfg, starts, N, n_wg, 1, 0.1)
+    plain = _run_batched(cfg, starts, N, n_wg, 1, 0.1, lds_limits=(0, 0))
     assert np.array_equal(staged[0], plain[0]), "tokens differ with staging"
     assert np.array_equal(staged[1], plain[1]), "logits differ with staging"
     assert np.array_equal(staged[2], plain[2]), "caches differ with staging"

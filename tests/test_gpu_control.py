@@ -1,10 +1,13 @@
 """Failure handling on the device, forced from the host.
 
-The host's stop word (mkd_abort) must end a running launch at whichever wait
-each workgroup is in, report MKD_E_ABORTED, and leave the model usable: the
-next launch from the same position decodes the same tokens as before.  No
-test here makes the device fault or hang: every device-side wait polls the
-stop word and its own watchdog deadline.
+The host's stop word (mkd_abort; Hyperkernel teardown, "Hardware fault
+detection and replanning": a stop word in the kernel's control block) must end
+a running launch at whichever wait each workgroup is in, report
+MKD_E_ABORTED, and leave the model usable: the next launch from the same
+position decodes the same tokens as before.  A stop asked for while nothing
+runs must not leak into the next launch.  No test here makes the device fault
+or hang: every device-side wait polls the stop word and its own watchdog
+deadline.
 """
 import pytest
 import torch
@@ -17,25 +20,32 @@ from tests.gpu_common import require_gpu, say
 pytestmark = pytest.mark.gpu
 
 
+def _tiny(max_seq, filled):
+    cfg = synth.TINY
+    w = synth.gen_weights(cfg, device="cuda")
+    kv = synth.gen_kv_cache(cfg, max_seq, filled, device="cuda")
+    return cfg, w, kv
+
+
 def test_abort_ends_a_running_launch_and_the_model_still_decodes():
     require_gpu()
-    cfg = synth.TINY
     T0, max_seq, long_n = 32, 4096, 4000
-    w = synth.gen_weights(cfg, device="cuda")
-    kv = synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")
+    cfg, w, kv = _tiny(max_seq, T0)
     dec = Decoder(cfg, w, kv, max_seq)
     first = int(synth.gen_tokens(1, cfg.vocab)[0])
     ref, _ = dec.decode(first, T0, 8, want_logits=False)
     ref = [int(x) for x in ref.cpu()]
     say(f"reference tokens {ref}")
 
+    # 4000 steps take far longer than the few microseconds between the
+    # enqueue and the stop request: the launch cannot finish first
     toks = torch.empty(long_n, dtype=torch.int32, device="cuda")
     dec.launch(first, T0, long_n, toks)
     capi.mkd_abort(dec.handle)
     st = capi.mkd_wait(dec.handle, 60000, raise_on_error=False)
-    say(f"stopped launch: code {st.code}")
-    # a launch that somehow finished before the stop word was read is fine too
-    assert st.code in (0, capi.MKD_E_ABORTED)
+    say(f"stopped launch: code {st.code} at workgroup {st.wg}, instruction {st.instr}, step {st.token}")
+    assert st.code == capi.MKD_E_ABORTED
+    assert 0 <= st.token < long_n
 
     again, _ = dec.decode(first, T0, 8, want_logits=False)
     again = [int(x) for x in again.cpu()]
@@ -44,15 +54,68 @@ def test_abort_ends_a_running_launch_and_the_model_still_decodes():
     dec.close()
 
 
+def test_abort_while_idle_does_not_stop_the_next_launch():
+    """mkd_abort on a handle with nothing in flight has no effect: the next
+    decode returns MKD_OK with the reference tokens (a leaking stop word
+    would end it through its own bounded wait with MKD_E_ABORTED instead)."""
+    require_gpu()
+    T0, max_seq = 32, 256
+    cfg, w, kv = _tiny(max_seq, T0)
+    dec = Decoder(cfg, w, kv, max_seq)
+    first = int(synth.gen_tokens(1, cfg.vocab)[0])
+    ref, _ = dec.decode(first, T0, 100, want_logits=False)
+    capi.mkd_abort(dec.handle)             # idle: after a completed, waited-for launch
+    toks = torch.empty(100, dtype=torch.int32, device="cuda")
+    dec.launch(first, T0, 100, toks)
+    st = capi.mkd_wait(dec.handle, 60000, raise_on_error=False)
+    say(f"launch after an idle abort: code {st.code}")
+    assert st.code == capi.MKD_OK
+    assert torch.equal(toks, ref)
+    dec.close()
+
+
+def test_second_launch_while_one_runs_is_rejected():
+    """A handle runs one launch at a time: a decode enqueued before the running
+    one was waited for is refused on the host (its buffer reset would clear
+    the running launch's flags), and the running launch completes normally."""
+    require_gpu()
+    T0, max_seq, n = 32, 4096, 3000
+    cfg, w, kv = _tiny(max_seq, T0)
+    dec = Decoder(cfg, w, kv, max_seq)
+    first = int(synth.gen_tokens(1, cfg.vocab)[0])
+    toks = torch.empty(n, dtype=torch.int32, device="cuda")
+    dec.launch(first, T0, n, toks)
+    other = torch.empty(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(capi.MkdError) as e:
+        dec.launch(first, T0, 4, other)
+    assert e.value.code == capi.MKD_E_INVALID
+    st = capi.mkd_wait(dec.handle, 60000, raise_on_error=False)
+    assert st.code == capi.MKD_OK
+    dec.close()
+
+
 def test_watchdog_setting_is_validated():
     require_gpu()
-    cfg = synth.TINY
-    w = synth.gen_weights(cfg, device="cuda")
-    kv = synth.gen_kv_cache(cfg, 64, 32, device="cuda")
+    cfg, w, kv = _tiny(64, 32)
     dec = Decoder(cfg, w, kv, 64)
     with pytest.raises(capi.MkdError):
         capi.mkd_set_watchdog(dec.handle, 0)
     capi.mkd_set_watchdog(dec.handle, 5000)
+    toks, _ = dec.decode(3, 32, 4, want_logits=False)
+    assert toks.numel() == 4
+    dec.close()
+
+
+def test_workspace_too_small_for_a_schedule_is_rejected():
+    """A schedule whose instruction tensor and activations do not fit in the
+    handle's workspace is refused on the host with the size it needs."""
+    require_gpu()
+    cfg, w, kv = _tiny(64, 32)
+    dec = Decoder(cfg, w, kv, 64, n_wg=8, n_chunks=1)
+    with pytest.raises(capi.MkdError) as e:
+        dec.rebuild(n_wg=256, n_chunks=8)  # a longer schedule and more split-KV partials
+    assert e.value.code == capi.MKD_E_INVALID and "workspace" in str(e.value)
+    dec.rebuild(n_wg=8, n_chunks=1)
     toks, _ = dec.decode(3, 32, 4, want_logits=False)
     assert toks.numel() == 4
     dec.close()
