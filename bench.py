@@ -1,10 +1,13 @@
 """Batch-1 decode benchmark of the persistent megakernel on one MI355X.
 
-A step is one decode launch of the workload: the Llama-3.2-1B-shaped model
-from a 128-position KV cache, 128 greedy decode steps (all opcodes of the
-path, every token), inputs already resident in HBM.  Prints one JSON line.
+A step is one decode launch of the workload: by default the
+Mixtral-8x7B-shaped top-2 MoE model (32 layers, d 4096, 8 experts of FFN
+14336, 93 GB of bf16 weights) from a 1024-position KV cache, 64 greedy decode
+steps (all opcodes of the path, every token), inputs already resident in HBM.
+It is the largest of the workloads, and one GPU holds it.  Prints one JSON
+line.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama1b --kv 128]
+    python bench.py [--steps K] [--warmup W] [--workload mixtral|llama1b|llama3b|llama1b_long --kv T]
 
 `value` is decode tokens/s; `roofline` prices the megakernel's algorithmic
 bytes (weights each step reads + K/V of the visible positions + the appended
@@ -26,7 +29,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "persistent_megakernel_decode_02_amd", "csrc", "mkd_kernel.hip")
+METRIC = "batch-1 decode tokens/s and % of HBM roofline (weight+KV bytes/token)"
+CSRC = os.path.join(ROOT, "persistent_megakernel_decode_02_amd", "csrc")
+# the device code of the kernels: a profile taken on other sources is stale
+KERNEL_SRCS = ["mkd_device.h", "mkd_internal.h", "mkd_kernel_dense.hip", "mkd_kernel_moe.hip",
+               "mkd_kernel_batch.hip", "mkd_launch.hip"]
 
 
 def log(*a):
@@ -34,7 +41,10 @@ def log(*a):
 
 
 def kernel_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload_key: str):
@@ -53,9 +63,15 @@ def measured_traffic(kernel: str, workload_key: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, T0: int, n_sample: int, first: int):
-    """The oracle as it stands, timed on this host: n_sample decode steps of
-    the same model from the same cache."""
+def cpu_baseline(cfg, T0: int, budget_s: float, first: int, w_gpu):
+    """The oracle as it stands, timed on this host: whole greedy decode steps
+    of the same model from the same cache, until budget_s is spent (at least
+    two).  Dense models: the oracle's own host copy of the weights, converted
+    once before timing.  The MoE model is too large for host memory as fp32:
+    the oracle keeps everything but the experts on the host and reads the two
+    routed experts of each layer back from the generated device tensors per
+    use (bit-identical to the host generator's), and that read is timed as
+    part of its step."""
     import numpy as np
     import synth
     from oracle import model as om
@@ -64,18 +80,30 @@ def cpu_baseline(cfg, T0: int, n_sample: int, first: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: generating host weights ({cfg.name})")
-    w = synth.gen_weights(cfg, device="cpu")
-    orc = om.Oracle(cfg, om.Weights.from_list(cfg, w))
-    kv = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + n_sample, T0))
-    orc.step(first, T0, kv)   # converts the weights once (not timed)
-    kv = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + n_sample, T0))
+    n_max = 4096
+    if cfg.is_moe:
+        names = [n for n, _ in synth.weight_specs(cfg)]
+        keep = [not (".gate." in n or ".up." in n or ".down." in n) for n in names]
+        wts = om.Weights(cfg, lambda i: w_gpu[i], cache=lambda i: keep[i])
+        how = "routed experts read back from the device per use"
+    else:
+        log(f"cpu baseline: generating host weights ({cfg.name})")
+        wts = om.Weights.from_list(cfg, synth.gen_weights(cfg, device="cpu"))
+        how = "host weights"
+    orc = om.Oracle(cfg, wts)
+    kv = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + n_max, T0))
+    orc.step(first, T0, kv)   # converts the kept weights once (not timed)
+    kv = om.kv_to_oracle(synth.gen_kv_cache(cfg, T0 + n_max, T0))
     t = time.perf_counter()
-    orc.decode(first, T0, n_sample, kv)
+    n, tok = 0, first
+    while n < n_max and (n < 2 or time.perf_counter() - t < budget_s):
+        tk, _ = orc.decode(tok, T0 + n, 1, kv)
+        tok = tk[0]
+        n += 1
     dt = time.perf_counter() - t
-    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_sample} greedy decode steps of the same model from the same "
-                      f"{T0}-position cache (numpy fp32, {dt:.1f}s)"}
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} greedy decode steps of the same model from the same {T0}-position cache "
+                      f"(numpy fp32, {how}, {dt:.1f}s)"}
 
 
 def calib_copy(n_bytes: int, reps: int) -> None:
@@ -96,16 +124,20 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5, help="timed decode launches")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama1b")
+    ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--kv", type=int, default=None, help="starting KV length (default: the workload's first)")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences decoded together (all from the same KV length)")
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--n-chunks", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=640,
-                    help="oracle decode steps timed on the host, 10-30 s (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="host time budget of the oracle sample: whole decode steps until it is spent "
+                         "(0 = skip)")
     ap.add_argument("--trace", action="store_true", help="per-opcode time breakdown (stderr)")
+    ap.add_argument("--trace-out", default=None, help="also write the breakdown to this markdown file")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="dispatch the grid without the cooperative flag (for profilers)")
     ap.add_argument("--calib-copy", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
 
@@ -139,14 +171,23 @@ def main() -> int:
 
     B = args.batch
     log(f"generating {cfg.name} weights and {B} {T0}-position KV cache(s) on the GPU")
-    w = synth.gen_weights(cfg, device="cuda")
+    tg = time.perf_counter()
+    n_t = len(synth.weight_specs(cfg))
+    w = []
+    for i in range(n_t):
+        w.append(synth.gen_weights(cfg, device="cuda", only=[i])[i])
+        if i % 64 == 63:
+            torch.cuda.synchronize()
+            log(f"  {i + 1}/{n_t} tensors, {time.perf_counter() - tg:.1f}s")
     if B == 1:
         kv = synth.gen_kv_cache(cfg, max_seq, T0, device="cuda")
     else:
         kv = torch.stack([synth.gen_kv_cache(cfg, max_seq, T0, seed=synth.SEED_KV + 101 * b, device="cuda")
                           for b in range(B)]).contiguous()
     torch.cuda.synchronize()
-    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B)
+    log(f"inputs generated in {time.perf_counter() - tg:.1f}s")
+    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B, cooperative=not args.plain_launch)
+    dec.trace_pos = T0
     log(f"schedule: n_wg={dec.n_wg} n_chunks={dec.n_chunks} max_instr={dec.max_instr} batch={B}")
     firsts = synth.gen_tokens(B, cfg.vocab)
     first = firsts[0]
@@ -181,17 +222,17 @@ def main() -> int:
     floor_us = roofline.floor_seconds(n_bytes) * 1e6 / N
 
     if args.trace:
-        trace_breakdown(dec, one, N)
+        trace_breakdown(dec, one, N, args.trace_out, f"{args.workload} KV {T0}, {N} steps per launch")
 
     cpu = None
-    if args.cpu_sample > 0:
-        cpu = cpu_baseline(cfg, T0, args.cpu_sample, first)
+    if args.cpu_seconds > 0 and B == 1:
+        cpu = cpu_baseline(cfg, T0, args.cpu_seconds, first, w)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
     key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
     kernel = "mkd_megakernel_batch" if B > 1 else ("mkd_megakernel_moe" if cfg.is_moe else "mkd_megakernel")
     traffic = measured_traffic(kernel, key)
     out = {
-        "metric": "batch-1 decode tokens/s" if B == 1 else f"batch-{B} decode tokens/s",
+        "metric": METRIC if B == 1 else f"batch-{B} decode tokens/s",
         "value": B * N * args.steps / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -205,6 +246,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} decoder, batch {B}, KV cache {T0} positions, {N} greedy "
                                f"decode steps per step (one launch)",
+                   "launch": "cooperative" if not args.plain_launch else "plain",
                    "weights": "bf16", "kv_cache": "bf16", "activations": "fp32",
                    "kv_start": T0, "decode_tokens_per_step": N, "n_wg": dec.n_wg,
                    "n_chunks": dec.n_chunks, "parallelism": "single GPU"},
@@ -222,68 +264,97 @@ def main() -> int:
     return 0
 
 
-def trace_breakdown(dec, launch_and_wait, N):
-    """Per-opcode time from the device trace (one extra traced launch)."""
+def stage_bytes(cfg, op: str, pos: int) -> int:
+    """Algorithmic HBM bytes of one stage of one layer at position pos (the
+    weights it reads, K/V of positions 0..pos for attention; the LM head's
+    per token) -- the per-opcode split of roofline.step_bytes."""
+    d, F, qd, kvd = cfg.d_model, cfg.d_ff, cfg.qd, cfg.kvd
+    return {"QKV": 2 * (qd + 2 * kvd) * d + 2 * d, "ATTN": 2 * kvd * 2 * (pos + 2), "AREDUCE": 0,
+            "OPROJ": 2 * d * qd, "UPGATE": 2 * 2 * F * d + 2 * d, "DOWN": 2 * d * F,
+            "MOE_UPGATE": 2 * (cfg.n_experts * d + 2 * 2 * F * d) + 2 * d, "MOE_DOWN": 2 * 2 * d * F,
+            "LMHEAD": 2 * cfg.vocab * d + 2 * d + 2 * d}.get(op, 0)
+
+
+def trace_breakdown(dec, launch_and_wait, N, out_path=None, title=""):
+    """Each opcode's cost from the device trace (one extra traced launch):
+    per instruction, the wait for inputs and the work after them; per stage,
+    its share of the token's critical path -- from the previous stage's last
+    publish to its own last publish, split into the transition (to its first
+    consumer ready), the spread of its consumers becoming ready, and its work
+    -- and the algorithmic bytes it moves in that time."""
     import numpy as np
     import torch
     from persistent_megakernel_decode_02_amd import capi
     words = dec.schedule
+    cfg = dec.cfg
     n_wg, max_instr = int(words[2]), int(words[4])
     tr = torch.zeros(n_wg * N * max_instr * 4, dtype=torch.int64, device="cuda")
     capi.mkd_set_trace(dec.handle, tr)
     launch_and_wait()
     capi.mkd_set_trace(dec.handle, None)
     hz = capi.mkd_clock_hz(dec.handle)
-    t = tr.cpu().numpy().reshape(n_wg, N, max_instr, 4)
+    us = 1e6 / hz
+    t = tr.cpu().numpy().reshape(n_wg, N, max_instr, 4).astype(np.float64)
     counts = words[16:16 + n_wg]
     body = words[16 + n_wg:].reshape(n_wg, max_instr, 16)
+    n_st = int(words[3])
     per_op = {}
+    pub = np.full((N, n_st), -np.inf)
+    rdy_min = np.full((N, n_st), np.inf)
+    rdy_max = np.full((N, n_st), -np.inf)
+    opname, layer_of = {}, {}
     for w in range(n_wg):
         for i in range(int(counts[w])):
             op = capi.OPCODE_NAMES.get(int(body[w, i, 0]), "?")
-            wait = (t[w, :, i, 1] - t[w, :, i, 0]).astype(np.float64) / hz * 1e6
-            work = (t[w, :, i, 2] - t[w, :, i, 1]).astype(np.float64) / hz * 1e6
-            has3 = t[w, :, i, 3] > 0
-            comp = np.where(has3, (t[w, :, i, 3] - t[w, :, i, 1]), 0).astype(np.float64) / hz * 1e6
-            per_op.setdefault(op, []).append((wait.mean(), work.mean(), comp.mean()))
-    log("per-opcode time per instruction (us; wait = start to inputs ready, work = ready to "
-        "published, of which comp = ready to end of the row stream):")
-    for op, v in sorted(per_op.items()):
-        v = np.array(v)
-        log(f"  {op:12s} n={len(v):5d} wait mean={v[:, 0].mean():8.2f} max={v[:, 0].max():8.2f}"
-            f"   work mean={v[:, 1].mean():8.2f} max={v[:, 1].max():8.2f}   comp mean={v[:, 2].mean():8.2f}")
-    # stage-to-stage latency: for each (step, stage), the last producer's
-    # publish time vs the first and last consumer's inputs-ready time
-    stage_of = body[..., 2]
-    n_st = int(words[3])
-    pub = np.full((N, n_st), -np.inf)
-    pub_min = np.full((N, n_st), np.inf)
-    rdy_min = np.full((N, n_st), np.inf)
-    rdy_max = np.full((N, n_st), -np.inf)
-    opname = {}
-    for w in range(n_wg):
-        for i in range(int(counts[w])):
-            st = int(stage_of[w, i])
-            opname[st] = capi.OPCODE_NAMES.get(int(body[w, i, 0]), "?")
+            st = int(body[w, i, 2])
+            opname[st], layer_of[st] = op, int(body[w, i, 1])
+            wait = (t[w, :, i, 1] - t[w, :, i, 0]) * us
+            work = (t[w, :, i, 2] - t[w, :, i, 1]) * us
+            per_op.setdefault(op, []).append(np.stack([wait, work], axis=1))
             pub[:, st] = np.maximum(pub[:, st], t[w, :, i, 2])
-            pub_min[:, st] = np.minimum(pub_min[:, st], t[w, :, i, 2])
             rdy_min[:, st] = np.minimum(rdy_min[:, st], t[w, :, i, 1])
             rdy_max[:, st] = np.maximum(rdy_max[:, st], t[w, :, i, 1])
-    lat, spread_pub, spread_rdy = {}, {}, {}
-    for st in range(1, n_st):
-        k = f"{opname[st - 1]}->{opname[st]}"
-        lat.setdefault(k, []).append(np.mean(rdy_min[:, st] - pub[:, st - 1]) / hz * 1e6)
-        spread_pub.setdefault(k, []).append(np.mean(pub[:, st - 1] - pub_min[:, st - 1]) / hz * 1e6)
-        spread_rdy.setdefault(k, []).append(np.mean(rdy_max[:, st] - rdy_min[:, st]) / hz * 1e6)
-    log("stage transitions (us): last publish -> first ready | producer publish spread | consumer ready spread")
-    for k in lat:
-        log(f"  {k:18s} {np.mean(lat[k]):7.2f} | {np.mean(spread_pub[k]):7.2f} | {np.mean(spread_rdy[k]):7.2f}")
-    # token time split: per-step makespan
-    starts = t[..., 0].astype(np.float64)
-    ends = t[..., 2].astype(np.float64)
-    valid = ends > 0
-    span = [(ends[:, s][valid[:, s]].max() - starts[:, s][valid[:, s]].min()) / hz * 1e6 for s in range(N)]
-    log(f"  traced step makespan: mean {np.mean(span):.1f} us")
+    lines = []
+    lines.append("Per instruction (us): wait = start to inputs ready; work = inputs ready to outputs published.")
+    lines.append("")
+    lines.append("| Opcode | Instructions | wait mean | wait max | work mean | work min | work max |")
+    lines.append("|---|---|---|---|---|---|---|")
+    for op, v in sorted(per_op.items()):
+        v = np.concatenate(v)
+        lines.append(f"| {op} | {len(v) // N} x {N} | {v[:, 0].mean():.2f} | {v[:, 0].max():.2f} | "
+                     f"{v[:, 1].mean():.2f} | {v[:, 1].min():.2f} | {v[:, 1].max():.2f} |")
+    # the critical path of each step, stage by stage
+    acc = {}
+    for k in range(N):
+        prev = np.min(t[:, k, 0, 0][counts > 0]) if k == 0 else pub[k - 1, n_st - 1]
+        for st in range(n_st):
+            op = opname[st]
+            p0 = prev if st == 0 else pub[k, st - 1]
+            a = acc.setdefault(op, np.zeros(5))
+            a[0] += (pub[k, st] - p0) * us                      # share of the critical path
+            a[1] += max(0.0, rdy_min[k, st] - p0) * us          # transition
+            a[2] += (rdy_max[k, st] - rdy_min[k, st]) * us      # consumer-ready spread
+            a[3] += (pub[k, st] - rdy_max[k, st]) * us          # work after the last consumer was ready
+            a[4] += stage_bytes(cfg, op, dec.trace_pos + k)
+    total = sum(a[0] for a in acc.values()) / N
+    lines.append("")
+    lines.append(f"Per token (us, mean over {N} steps): each stage's share of the critical path (previous stage's "
+                 "last publish to its own last publish) = transition (to its first consumer ready) + ready spread "
+                 "+ work; bytes are its algorithmic HBM bytes, GB/s = bytes / share.")
+    lines.append("")
+    lines.append("| Opcode | share us/token | % | transition | ready spread | work | MB/token | GB/s | % of 8 TB/s |")
+    lines.append("|---|---|---|---|---|---|---|---|---|")
+    for op, a in sorted(acc.items(), key=lambda kv: -kv[1][0]):
+        a = a / N
+        gbs = a[4] / (a[0] * 1e-6) / 1e9 if a[0] > 0 else 0.0
+        lines.append(f"| {op} | {a[0]:.1f} | {100 * a[0] / total:.1f} | {a[1]:.1f} | {a[2]:.1f} | {a[3]:.1f} | "
+                     f"{a[4] / 1e6:.1f} | {gbs:.0f} | {100 * gbs / 8000:.1f} |")
+    lines.append(f"| total | {total:.1f} | 100 | | | | | | |")
+    for ln in lines:
+        log(ln)
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(f"# Per-opcode cost: {title}\n\n" + "\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":
