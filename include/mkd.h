@@ -210,6 +210,30 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
                    void* kv_cache, int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes,
                    int32_t* host_control, int32_t device, mkd_model** out);
 
+/* Size of the device workspace that mkd_init_static uses: a static array
+ * inside the library, one copy per GPU, held until the process ends. */
+#define MKD_STATIC_WORKSPACE_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: mkd_init
+ * (one sequence) with no workspace argument.  The handle's workspace is the
+ * library's static array on `device` (MKD_STATIC_WORKSPACE_BYTES); nothing is
+ * allocated, by this call or by the build, load and decode calls on the
+ * handle.  The caller still passes weights, KV cache, the pinned host control
+ * block and the outputs, as for mkd_init.
+ * Limits: the tables and each schedule loaded later must fit in the static
+ * size (init: MKD_E_INVALID naming the bytes max_seq needs; schedule build or
+ * load: MKD_E_INVALID naming the bytes the schedule needs).  One handle holds
+ * a device's array at a time: a second mkd_init_static on the same device
+ * fails with MKD_E_INVALID until the first handle is destroyed.  The array
+ * keeps the last handle's contents; init rewrites its tables and every launch
+ * clears the activations and status first.  Launches on the handle are
+ * serialised like any handle's (a second decode while one runs is refused);
+ * launches of other processes have their own copy.
+ * Errors otherwise as mkd_init. */
+int mkd_init_static(const mkd_config* cfg, const void* const* weights, size_t n_weights,
+                    void* kv_cache, int32_t max_seq, int32_t* host_control, int32_t device, mkd_model** out);
+
 /* Query the device's compute-unit count and the largest grid a cooperative
  * launch of the megakernel can hold on it: one block per compute unit, all
  * resident at once, as a grid-wide wait requires (Hyperkernel teardown,

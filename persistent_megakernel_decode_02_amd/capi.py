@@ -35,7 +35,7 @@ OPCODE_NAMES = {1: "QKV", 2: "ATTN", 3: "AREDUCE", 4: "OPROJ", 5: "UPGATE", 6: "
 EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_count",
            "mkd_weight_shape", "mkd_kv_cache_bytes", "mkd_schedule_build",
            "mkd_schedule_build_batch", "mkd_schedule_validate", "mkd_default_chunks",
-           "mkd_workspace_bytes", "mkd_workspace_layout", "mkd_init", "mkd_init_batch",
+           "mkd_workspace_bytes", "mkd_workspace_layout", "mkd_init", "mkd_init_batch", "mkd_init_static",
            "mkd_device_info", "mkd_lds_plan", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
            "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
            "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_set_lds_limits",
@@ -44,6 +44,7 @@ EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_coun
 # regions of a workspace, in mkd_workspace_layout's order
 WORKSPACE_REGIONS = ("wtab", "rope", "status", "zero", "schedule", "activations", "flags", "total")
 CONTROL_WORDS = 16   # int32 words of the pinned host control block
+STATIC_WORKSPACE_BYTES = 16 << 20   # MKD_STATIC_WORKSPACE_BYTES
 
 
 class mkd_config(ctypes.Structure):
@@ -99,6 +100,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_init": ([cfgp, ctypes.POINTER(P), SZ, P, I32, P, SZ, P, I32, ctypes.POINTER(P)], ctypes.c_int),
         "mkd_init_batch": ([cfgp, ctypes.POINTER(P), SZ, P, I32, I32, P, SZ, P, I32, ctypes.POINTER(P)],
                            ctypes.c_int),
+        "mkd_init_static": ([cfgp, ctypes.POINTER(P), SZ, P, I32, P, I32, ctypes.POINTER(P)], ctypes.c_int),
         "mkd_device_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_lds_plan": ([cfgp, I32, I32, I32, I32, ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_build_schedule": ([P, I32, I32, P, SZ, ctypes.POINTER(SZ)], ctypes.c_int),
@@ -230,6 +232,15 @@ def mkd_init_batch(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, b
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().mkd_init_batch(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, batch,
                                  _ptr(workspace), nbytes, _ptr(control), device, ctypes.byref(h)))
+    return h.value
+
+
+def mkd_init_static(cfg: mkd_config, weights: Sequence, kv_cache, max_seq: int, control, device: int = 0) -> int:
+    """As mkd_init, with the library's static per-device workspace (no workspace argument)."""
+    arr = (ctypes.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    h = ctypes.c_void_p()
+    _check(load().mkd_init_static(ctypes.byref(cfg), arr, len(weights), _ptr(kv_cache), max_seq, _ptr(control),
+                                  device, ctypes.byref(h)))
     return h.value
 
 

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -78,6 +79,7 @@ struct mkd_model {
   int flag_stride = 0;
   int x_cap = 0, pre_cap = -1;     // mkd_set_lds_limits
   bool plain_launch = false;       // mkd_set_launch_mode
+  bool static_ws = false;          // the workspace is the library's static array (mkd_init_static)
   hipEvent_t done = nullptr;
   hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
   bool launched = false, timed = false;
@@ -294,9 +296,11 @@ int mkd_init(const mkd_config* cfg, const void* const* weights, size_t n_weights
                         device, out);
 }
 
-int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
-                   int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes, int32_t* host_control,
-                   int32_t device, mkd_model** out) {
+// mkd_init_batch and mkd_init_static; static_ws: the workspace is this
+// library's static array on `device` (already known to be device memory)
+static int init_common(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
+                       int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes,
+                       int32_t* host_control, int32_t device, bool static_ws, mkd_model** out) {
   if (!out) return fail(MKD_E_INVALID, "null out");
   *out = nullptr;
   if (batch < 1 || batch > kMaxBatch) return fail(MKD_E_INVALID, "batch must be in [1, 8]");
@@ -323,8 +327,10 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   if (!workspace || ((uintptr_t)workspace & (kWsAlign - 1)))
     return fail(MKD_E_INVALID, "workspace null or not 256-byte aligned");
   if (workspace_bytes < L.fixed)
-    return fail(MKD_E_INVALID, "workspace of " + std::to_string(workspace_bytes) + " bytes is smaller than the " +
-                                   std::to_string(L.fixed) + " its tables need (mkd_workspace_bytes sizes it)");
+    return fail(MKD_E_INVALID, std::string(static_ws ? "the static workspace" : "workspace") + " of " +
+                                   std::to_string(workspace_bytes) + " bytes is smaller than the " +
+                                   std::to_string(L.fixed) + " its tables need at max_seq " + std::to_string(max_seq) +
+                                   (static_ws ? "" : " (mkd_workspace_bytes sizes it)"));
   if (!host_control || ((uintptr_t)host_control & 63))
     return fail(MKD_E_INVALID, "host_control null or not 64-byte aligned");
 
@@ -341,8 +347,8 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   // the borrowed memory must be what the kernel can reach: device memory of
   // this device, and pinned (device-mapped) host memory for the control block
   hipPointerAttribute_t at{};
-  if (hipPointerGetAttributes(&at, workspace) != hipSuccess || at.type != hipMemoryTypeDevice ||
-      at.device != device) {
+  if (!static_ws && (hipPointerGetAttributes(&at, workspace) != hipSuccess || at.type != hipMemoryTypeDevice ||
+                     at.device != device)) {
     (void)hipGetLastError();
     return fail(MKD_E_INVALID, "workspace is not device memory of device " + std::to_string(device));
   }
@@ -410,6 +416,42 @@ int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_w
   if ((e = hipEventCreate(&m->k0)) != hipSuccess || (e = hipEventCreate(&m->k1)) != hipSuccess)
     return cleanup(MKD_E_HIP, "hipEventCreate");
   *out = m;
+  return MKD_OK;
+}
+
+int mkd_init_batch(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
+                   int32_t max_seq, int32_t batch, void* workspace, size_t workspace_bytes, int32_t* host_control,
+                   int32_t device, mkd_model** out) {
+  return init_common(cfg, weights, n_weights, kv_cache, max_seq, batch, workspace, workspace_bytes, host_control,
+                     device, false, out);
+}
+
+namespace {
+// the handle that holds each device's static workspace (null: free)
+std::mutex g_static_mu;
+mkd_model* g_static_owner[64] = {};
+}  // namespace
+
+int mkd_init_static(const mkd_config* cfg, const void* const* weights, size_t n_weights, void* kv_cache,
+                    int32_t max_seq, int32_t* host_control, int32_t device, mkd_model** out) {
+  if (!out) return fail(MKD_E_INVALID, "null out");
+  *out = nullptr;
+  if (device < 0 || device >= 64) return fail(MKD_E_INVALID, "device index out of range");
+  hipError_t e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_owner[device])
+    return fail(MKD_E_INVALID, "the static workspace of device " + std::to_string(device) +
+                                   " is held by another handle (mkd_destroy it first)");
+  void* ws = nullptr;
+  const char* why = "";
+  int rc = static_workspace(device, &ws, &why);
+  if (rc) return fail(rc, why);
+  rc = init_common(cfg, weights, n_weights, kv_cache, max_seq, 1, ws, kStaticWorkspaceBytes, host_control, device,
+                   true, out);
+  if (rc) return rc;
+  (*out)->static_ws = true;
+  g_static_owner[device] = *out;
   return MKD_OK;
 }
 
@@ -644,7 +686,8 @@ static int upload_schedule(mkd_model* m, const int32_t* words, size_t n) {
   ws_schedule(c, words, n, &L);
   if (L.total > m->ws_bytes)
     return fail(MKD_E_INVALID, "this schedule needs a workspace of " + std::to_string(L.total) + " bytes, the handle has " +
-                                   std::to_string(m->ws_bytes) + " (mkd_workspace_bytes sizes it)");
+                                   std::to_string(m->ws_bytes) +
+                                   (m->static_ws ? " (the static workspace's fixed size)" : " (mkd_workspace_bytes sizes it)"));
   hipError_t e = hipSetDevice(m->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
   if (m->launched) hipEventSynchronize(m->done);
@@ -872,6 +915,10 @@ void mkd_destroy(mkd_model* m) {
   if (!m) return;
   hipSetDevice(m->device);
   if (m->launched && m->done) hipEventSynchronize(m->done);
+  if (m->static_ws) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (g_static_owner[m->device] == m) g_static_owner[m->device] = nullptr;
+  }
   if (m->done) hipEventDestroy(m->done);
   if (m->k0) hipEventDestroy(m->k0);
   if (m->k1) hipEventDestroy(m->k1);

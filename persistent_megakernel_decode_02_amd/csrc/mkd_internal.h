@@ -124,6 +124,10 @@ int launch(const KParams& p, size_t ll_words, void* stream, void* ev0, void* ev1
 // co-resident workgroups of the persistent kernel for `batch` sequences of a
 // dense or MoE model
 int max_coop_blocks(int device, size_t lds, int batch, bool moe, int* out);
+// The static workspace of mkd_init_static (device address of this device's
+// copy; the device must be current)
+constexpr size_t kStaticWorkspaceBytes = (size_t)MKD_STATIC_WORKSPACE_BYTES;
+int static_workspace(int device, void** ptr, const char** why);
 // host-side handles of the persistent kernels (one translation unit each)
 const void* kernel_dense();
 const void* kernel_moe();

@@ -6,9 +6,48 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mkd_internal.h"
 
 namespace mkd {
+
+// The workspace of handles made by mkd_init_static: a device array of this
+// library, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a
+// stand-in): it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_workspace(int device, void** ptr, const char** why) {
+  if (device < 0 || device >= kMaxDevices) {
+    *why = "device index out of range for the static workspace";
+    return MKD_E_INVALID;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess || cur != device) {
+      *why = "the handle's device must be current when its static workspace is looked up";
+      return MKD_E_HIP;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *why = "hipGetSymbolAddress of the static workspace failed";
+      return MKD_E_HIP;
+    }
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return MKD_OK;
+}
 
 extern "C" __global__ void mkd_reset(uint64_t* ll, size_t n, int32_t* status) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
