@@ -138,6 +138,9 @@ def main() -> int:
     ap.add_argument("--trace-out", default=None, help="also write the breakdown to this markdown file")
     ap.add_argument("--plain-launch", action="store_true",
                     help="dispatch the grid without the cooperative flag (for profilers)")
+    ap.add_argument("--staged-units", type=int, default=-1,
+                    help="cap on the weight units per wavefront staged ahead in LDS (-1: no cap; 0 turns "
+                         "staging, and for MoE the expert prediction, off)")
     ap.add_argument("--calib-copy", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
 
@@ -186,7 +189,8 @@ def main() -> int:
                           for b in range(B)]).contiguous()
     torch.cuda.synchronize()
     log(f"inputs generated in {time.perf_counter() - tg:.1f}s")
-    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B, cooperative=not args.plain_launch)
+    dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B, cooperative=not args.plain_launch,
+                  lds_limits=None if args.staged_units < 0 else (0, args.staged_units))
     dec.trace_pos = T0
     log(f"schedule: n_wg={dec.n_wg} n_chunks={dec.n_chunks} max_instr={dec.max_instr} batch={B}")
     firsts = synth.gen_tokens(B, cfg.vocab)
@@ -228,6 +232,11 @@ def main() -> int:
     if args.cpu_seconds > 0 and B == 1:
         cpu = cpu_baseline(cfg, T0, args.cpu_seconds, first, w)
         log(f"cpu baseline: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+    spec = None
+    if cfg.is_moe:
+        hits, preds = capi.mkd_spec_stats(dec.handle)
+        spec = {"hits": hits, "predictions": preds, "hit_rate": hits / preds if preds else None}
+        log(f"expert prediction: {hits} of {preds} gate/up tiles had their routed expert predicted")
     key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
     kernel = "mkd_megakernel_batch" if B > 1 else ("mkd_megakernel_moe" if cfg.is_moe else "mkd_megakernel")
     traffic = measured_traffic(kernel, key)
@@ -247,6 +256,7 @@ def main() -> int:
         "config": {"workload": f"{cfg.name} decoder, batch {B}, KV cache {T0} positions, {N} greedy "
                                f"decode steps per step (one launch)",
                    "launch": "cooperative" if not args.plain_launch else "plain",
+                   "expert_prediction": spec,
                    "weights": "bf16", "kv_cache": "bf16", "activations": "fp32",
                    "kv_start": T0, "decode_tokens_per_step": N, "n_wg": dec.n_wg,
                    "n_chunks": dec.n_chunks, "parallelism": "single GPU"},

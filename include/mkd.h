@@ -248,8 +248,9 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg);
  * wavefront (1 KiB each), offset of those units inside the input area
  * (0 = an area of their own after the others), total bytes}.  The staged
  * units are the next instruction's weights loaded ahead of it (epic-kernel
- * README, "L2 prefetching overlapped with prior instructions"): dense
- * gate/up rows, loaded while the workgroup waits out the attention phase.
+ * README, "L2 prefetching overlapped with prior instructions"), while the
+ * workgroup waits out the attention phase: dense gate/up rows, or for MoE
+ * models the predicted expert's gate/up rows (mkd_spec_stats).
  * MKD_E_INVALID for a bad config or argument. */
 int mkd_lds_plan(const mkd_config* cfg, int32_t batch, int32_t n_wg, int32_t n_chunks, int32_t lds_max,
                  int32_t* out);
@@ -346,6 +347,20 @@ int mkd_kernel_ms(mkd_model* m, float* ms);
 /* Wall-clock tick rate of the device in Hz (for trace and watchdog).
  * Plumbing. */
 int mkd_clock_hz(mkd_model* m, double* hz);
+
+/* Speculative expert prediction of the last launch mkd_wait saw end (MoE
+ * models; epic-kernel README, "Speculative expert prediction": the top-2
+ * experts are predicted from the pre-attention residual before the router
+ * runs, and the predicted experts' weights are loaded early).  Here every
+ * workgroup scores the router on the layer's pre-attention residual after its
+ * QKV rows, and the instruction before its gate/up tile stages the predicted
+ * expert's first rows of that tile in LDS.  The real router always decides:
+ * a tile whose routed expert was predicted starts from the staged rows, any
+ * other streams all of its rows, so the result never depends on the
+ * prediction.  *predictions: gate/up tiles that had a prediction; *hits:
+ * those whose routed expert it named.  Both 0 for dense models or when
+ * staging is off (mkd_set_lds_limits with max_staged_units 0). */
+int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions);
 
 /* Limits on the per-workgroup LDS plan of schedules built or loaded after
  * this call: the batched input area in floats (0 = no limit; rounded down to

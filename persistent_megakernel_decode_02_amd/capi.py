@@ -38,7 +38,7 @@ EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_coun
            "mkd_workspace_bytes", "mkd_workspace_layout", "mkd_init", "mkd_init_batch", "mkd_init_static",
            "mkd_device_info", "mkd_lds_plan", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
            "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
-           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_set_lds_limits",
+           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_spec_stats", "mkd_set_lds_limits",
            "mkd_set_launch_mode", "mkd_destroy")
 
 # regions of a workspace, in mkd_workspace_layout's order
@@ -113,6 +113,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_set_trace": ([P, P, SZ], ctypes.c_int),
         "mkd_kernel_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mkd_clock_hz": ([P, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "mkd_spec_stats": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_set_lds_limits": ([P, I32, I32], ctypes.c_int),
         "mkd_set_launch_mode": ([P, I32], ctypes.c_int),
         "mkd_destroy": ([P], None),
@@ -328,6 +329,13 @@ def mkd_clock_hz(m: int) -> float:
     hz = ctypes.c_double()
     _check(load().mkd_clock_hz(m, ctypes.byref(hz)))
     return hz.value
+
+
+def mkd_spec_stats(m: int):
+    """(hits, predictions) of the last waited-for launch's expert predictions."""
+    h, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().mkd_spec_stats(m, ctypes.byref(h), ctypes.byref(n)))
+    return h.value, n.value
 
 
 def mkd_set_lds_limits(m: int, max_input_floats: int = 0, max_staged_units: int = -1) -> None:

@@ -80,6 +80,7 @@ struct mkd_model {
   int x_cap = 0, pre_cap = -1;     // mkd_set_lds_limits
   bool plain_launch = false;       // mkd_set_launch_mode
   bool static_ws = false;          // the workspace is the library's static array (mkd_init_static)
+  int32_t spec_hit = 0, spec_n = 0;  // expert predictions of the last waited-for launch
   hipEvent_t done = nullptr;
   hipEvent_t k0 = nullptr, k1 = nullptr;  // timing events around the megakernel
   bool launched = false, timed = false;
@@ -558,7 +559,16 @@ constexpr size_t kLdsSlack = 256;  // static LDS of the kernel and a margin
 // that the passes can be exercised on small models.
 static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int batch, int lds_max,
                   const LdsCaps& caps) {
-  if (batch == 1) return;
+  if (batch == 1) {
+    // MoE: the input area grows to the LDS left over; its part past the
+    // O-projection's and gate/up's inputs holds the predicted expert's rows
+    if (c->n_experts == 0 || lds_max <= 0) return;
+    const size_t other = lds_bytes(p) - (size_t)p.x_floats * sizeof(float);
+    if (other + kLdsSlack >= (size_t)lds_max) return;
+    const int fill = (int)(((size_t)lds_max - kLdsSlack - other) / sizeof(float)) & ~3;
+    if (fill > p.x_floats) p.x_floats = fill;
+    return;
+  }
   if (caps.x_cap > 0) {
     const int seg = 64 * (8 * batch + 4);   // one 512-element segment of every sequence, padded
     const int cap = caps.x_cap / seg * seg;
@@ -589,6 +599,23 @@ static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int b
 // projection's longer input reuses that space after gate/up has read them.
 static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max, const LdsCaps& caps) {
   p.pre_off = 0;
+  if (batch == 1 && c->n_experts > 0) {
+    // MoE: the predicted expert's first gate/up rows, in the input area past
+    // the O-projection's and gate/up's inputs (the down projection's two-expert
+    // input reuses it afterwards); only where the router scoring of the
+    // prediction has its fast form (one expert row per wavefront, d <= 4096)
+    p.pre_units = 0;
+    if (c->n_experts > kWaves || c->d_model > 4096) return;
+    const int qd = c->n_q_heads * c->head_dim;
+    const int off = (std::max(vec_floats(c->d_model, 1), vec_floats(qd, 1)) + 3) & ~3;
+    if (off >= p.x_floats) return;
+    int n = std::min((p.x_floats - off) / (kWaves * 256), kPreMax);
+    if (caps.pre_cap >= 0 && caps.pre_cap < n) n = caps.pre_cap;
+    if (n < 1) return;
+    p.pre_off = off;
+    p.pre_units = n;
+    return;
+  }
   if (batch == 1) {
     p.pre_units = pre_units_for(c, lds_bytes(p), lds_max, caps);
     return;
@@ -850,6 +877,8 @@ int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out) {
   if (e != hipSuccess) return hip_fail(e, "read status");
   m->launched = false;
   __atomic_store_n(m->h_ctrl, 0, __ATOMIC_SEQ_CST);
+  m->spec_hit = st[S_SPEC_HIT];
+  m->spec_n = st[S_SPEC_N];
   if (out) *out = mkd_status{st[S_CODE], st[S_WG], st[S_INSTR], st[S_TOKEN]};
   if (st[S_CODE] != MKD_OK) {
     return fail(st[S_CODE], "device reported error " + std::to_string(st[S_CODE]) + " at workgroup " +
@@ -872,6 +901,13 @@ int mkd_set_lds_limits(mkd_model* m, int32_t max_input_floats, int32_t max_stage
   if (max_input_floats < 0 || max_staged_units < -1) return fail(MKD_E_INVALID, "limits out of range");
   m->x_cap = max_input_floats;
   m->pre_cap = max_staged_units;
+  return MKD_OK;
+}
+
+int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions) {
+  if (!m || !hits || !predictions) return fail(MKD_E_INVALID, "null argument");
+  *hits = m->spec_hit;
+  *predictions = m->spec_n;
   return MKD_OK;
 }
 

@@ -405,9 +405,6 @@ __device__ __forceinline__ void mark_ready(Ctx& c) {
   if (c.tr && c.tid == 0) st_u64(c.tr + 1, wall_clock64());
 }
 
-__device__ __forceinline__ void mark_computed(Ctx& c) {
-  if (c.tr && c.tid == 0) st_u64(c.tr + 3, wall_clock64());
-}
 
 // sum of v over the workgroup (all threads call; result in all threads)
 __device__ __forceinline__ float block_sum(Ctx& c, float v) {
@@ -473,6 +470,66 @@ __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, u
 template <int K, class M = InPlace, int S0 = 8>
 __device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K], M m = M()) {
   return gather<K, M, S0>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count, m);
+}
+
+// Stage small inputs without waiting for the producing stage's flags: every
+// thread re-reads its words (one 16-byte load per pair of words, pairs
+// tid, tid + kThreads, ...) until each carries the expected tag.  The
+// instruction then waits only for the producers of the words it reads -- an
+// attention instruction for the few QKV tiles that hold its head's q, k and
+// v rows, a split-KV reduction for its head's chunk partials -- and saves the
+// round trip of the flag poll.  Only for inputs of at most kThreads * S word
+// pairs read by few instructions: the reads repeat until the data is there.
+// The abort word, stop word and deadline are looked at every 32 rounds, by
+// each wavefront as a whole.
+template <int S>
+__device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
+  CKParams& p = c.p;
+  const Span sp = span_of(src, n);
+  unsigned pending = 0;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int i0 = 2 * (k * kThreads + c.tid) - sp.lead;
+    if (i0 >= 0 && i0 < n) pending |= 1u << (2 * k);
+    if (i0 + 1 >= 0 && i0 + 1 < n) pending |= 2u << (2 * k);
+  }
+  const uint64_t t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+    Staged<S> st;
+    ll_issue<S>(c, sp, 0, st);
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int i0 = 2 * (k * kThreads + c.tid) - sp.lead;
+      if ((pending & (1u << (2 * k))) && st.v[k].y == tag) {
+        dst[i0] = __uint_as_float(st.v[k].x);
+        pending &= ~(1u << (2 * k));
+      }
+      if ((pending & (2u << (2 * k))) && st.v[k].w == tag) {
+        dst[i0 + 1] = __uint_as_float(st.v[k].z);
+        pending &= ~(2u << (2 * k));
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pending != 0) == 0) return true;   // this wavefront's words are in
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 31) == 31) {
+      int stop = 0;
+      if (c.sflag[0] || __hip_atomic_load(&p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        stop = 1;
+      } else if (__hip_atomic_load(p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+        stop = 2;
+      } else if (wall_clock64() - t0 > p.watchdog_ticks) {
+        stop = 3;
+      }
+      stop = uni(stop);
+      if (stop) {
+        if (c.lane == 0) {
+          if (stop == 1) c.sflag[0] = 1;
+          else raise_error(c, stop == 2 ? MKD_E_ABORTED : MKD_E_WATCHDOG, true);
+        }
+        return false;
+      }
+    }
+  }
 }
 
 // RMSNorm gains of this thread's elements (i = tid + k * kThreads), read
@@ -709,6 +766,8 @@ __device__ __forceinline__ int wave_rows(int nrows, int w) {
   return nrows > w ? (nrows - w + kWaves - 1) / kWaves : 0;
 }
 
+
+
 // Rows of one GEMV instruction, described by data so that every dense
 // opcode runs the same code (one copy of the streaming loop keeps the hot
 // code inside the instruction cache).  Output row r in [a, a + nrows) has R
@@ -822,7 +881,7 @@ __device__ __forceinline__ void desc_upgate(CKParams& p, int l, GemvDesc& g) {
   g.K = p.d;
 }
 
-// LDS staging area of this wavefront's gate/up units, after the reduction scratch
+// LDS staging area of this wavefront's weight units, after the reduction scratch
 __device__ __forceinline__ u32x4* pre_area(Ctx& c) {
   return (u32x4*)(c.red + kRed) + (size_t)c.wave * c.p.pre_units * 64;
 }
@@ -831,11 +890,16 @@ __device__ __forceinline__ u32x4* pre_area(Ctx& c) {
 // [a, b) of layer l in LDS, as many whole rows as pre_units units (1 KiB,
 // one 16-byte load per lane) hold: 16-byte loads that write LDS
 // directly (lane i's bytes land at 16 i of the unit's 1 KiB), issued while the
-// workgroup has nothing else in its load queue.  Rows are read through
-// descriptors that span exactly the row, as in the streamer.  The wavefront
-// waits for its staging loads here: it is about to wait microseconds for its
-// next inputs anyway, and while such loads are outstanding the compiler makes
-// every later LDS access wait for all vector memory operations.
+// workgroup has nothing else in its load queue (the next instruction's weights
+// loaded ahead of it, epic-kernel README, "L2 prefetching overlapped with
+// prior instructions").  Rows are read through descriptors that span exactly
+// the row, as in the streamer.  The wavefront waits for its staging loads
+// here: it is about to wait microseconds for its next inputs anyway, and while
+// such loads are outstanding the compiler makes every later LDS access wait
+// for all vector memory operations.  (Staging the down projection's rows at
+// the end of gate/up, and the LM head's at the end of the last down
+// projection, was measured slower: every workgroup then loads at once and
+// starts waiting for its inputs only after those loads.)
 __device__ __forceinline__ void stage_upgate(Ctx& c, int l, int a, int b) {
   CKParams& p = c.p;
   GemvDesc g;
@@ -990,7 +1054,6 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
   if (gamma) rmsnorm_g(c, p.d, gamma, gr);
   // staged units were written by this wavefront, which waited for them
   rs.run(c.xs, c.out, pre_area(c));
-  mark_computed(c);
   __syncthreads();
   gemv_epilogue<1>(c, op, l, a, b, index, tag);
   return true;
@@ -1171,7 +1234,6 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
     for (int h = 0; h < RROWS; ++h)                 // drain
       if (q0 + h < nq) c.out[m.slot(npre + q0 + h)] = dot_row(ring[h]);
   }
-  mark_computed(c);
   __syncthreads();
   gemv_epilogue<1>(c, op, l, a, b, index, tag);
   return true;
@@ -1518,7 +1580,6 @@ __device__ __forceinline__ bool op_gemv_b(Ctx& c, int op, int l, int a, int b, i
     next.prefetch_rest();
     next.run(c.xs, c.out, true);
   }
-  mark_computed(c);
   __syncthreads();
   bs.combine(c, c.out);
   gemv_epilogue<NB>(c, op, l, a, b, index, tag);
@@ -1587,6 +1648,112 @@ __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b,
 }
 
 // ---------------------------------------------------------------- opcodes: MoE
+
+// Speculative expert prediction (epic-kernel README, "Speculative expert
+// prediction": the top-2 experts are predicted from the pre-attention
+// residual before the router runs, and the predicted experts' weights are
+// loaded early).  LDS words of the prediction and of its outcome counts.
+constexpr int kPredA = 5, kPredB = 6, kStagedExpert = 7;   // sflag words
+constexpr int kSpecHitWord = 252, kSpecNWord = 253;         // int words of the reduction scratch
+
+// The expert whose gate/up rows the tile [a, b) of a layer's stacked
+// (expert a, expert b) rows reads, given the two experts; -1 if the tile
+// straddles both
+__device__ __forceinline__ int tile_expert(CKParams& p, int a, int b, int ea, int eb) {
+  return b <= p.F ? ea : (a >= p.F ? eb : -1);
+}
+
+// The stream map of this wavefront's gate/up rows of MoE tile [a, b) of
+// layer l for experts (ea, eb): output row r < F is expert ea's row r, else
+// expert eb's row r - F; streamed rows alternate gate and up
+__device__ __forceinline__ void desc_moe_upgate(CKParams& p, int l, int a, int w, int ea, int eb, GemvDesc& g) {
+  g.b00 = lptr(p, l, WL_EXPERTS + ea); g.b01 = lptr(p, l, WL_EXPERTS + eb); g.b02 = nullptr;
+  g.b10 = lptr(p, l, WL_EXPERTS + p.E + ea); g.b11 = lptr(p, l, WL_EXPERTS + p.E + eb); g.b12 = nullptr;
+  g.s1 = p.F; g.s2 = kNoSplit; g.K = p.d; g.R = 2; g.xoff1 = 0; g.a = a; g.w = w;
+}
+
+// After the layer's QKV rows, while xs still holds the layer's input
+// residual h (the QKV streamers keep their normalised copy in registers):
+// score the router on rmsnorm(h) with the FFN norm's gains -- one expert row
+// per wavefront -- and keep the top two (same order and tie rule as the
+// router) in LDS.  xs is free to overwrite: the next instructions fetch their
+// own inputs.
+__device__ __forceinline__ void predict_experts(Ctx& c, int l) {
+  CKParams& p = c.p;
+  const uint16_t* gamma = lptr(p, l, WL_FFN_NORM);
+  const Gains gr = load_gains(c, p.d, gamma);
+  constexpr int RU = 8;
+  const uint16_t* wr = lptr(p, l, WL_ROUTER);
+  const bool mine = c.wave < p.E;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(wr + (size_t)(mine ? c.wave : 0) * p.d, mine ? (uint32_t)p.d * 2u : 0u);
+  u32x4 rw[RU];
+#pragma unroll
+  for (int k = 0; k < RU; ++k) rw[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (k * 64 + c.lane) * 16, 0, 0);
+  __syncthreads();                        // every wavefront is done with its QKV rows
+  rmsnorm_g(c, p.d, gamma, gr);
+  if (p.d & 511) {
+    pad_zero(c, c.xs, p.d);
+    __syncthreads();
+  }
+  if (mine) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < RU; ++k) {
+      const int i0 = (k * 64 + c.lane) * 8;
+      if (i0 < p.d) {
+        const uint32_t wv[4] = {rw[k].x, rw[k].y, rw[k].z, rw[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(bf_lo(wv[j]), c.xs[i0 + 2 * j], acc);
+          acc = fmaf(bf_hi(wv[j]), c.xs[i0 + 2 * j + 1], acc);
+        }
+      }
+    }
+    const float z = wave_sum(acc);
+    if (c.lane == 0) c.red[64 + c.wave] = z;
+  }
+  __syncthreads();
+  if (c.tid == 0) {
+    int ea = 0;
+    for (int e = 1; e < p.E; ++e)
+      if (c.red[64 + e] > c.red[64 + ea]) ea = e;
+    int eb = ea == 0 ? 1 : 0;
+    for (int e = 0; e < p.E; ++e)
+      if (e != ea && c.red[64 + e] > c.red[64 + eb]) eb = e;
+    c.sflag[kPredA] = ea;
+    c.sflag[kPredB] = eb;
+  }
+  __syncthreads();
+}
+
+// Stage the first units of this wavefront's stream of the MoE gate/up tile
+// [a, b) of layer l for the predicted experts, in the input area past the
+// gate/up input (pre_area_b), and record which expert they belong to.  As
+// stage_upgate: issued while the workgroup waits out the attention phase, and
+// waited for on the spot.
+__device__ __forceinline__ void stage_predicted(Ctx& c, int l, int a, int b) {
+  CKParams& p = c.p;
+  const int pa = uni(c.sflag[kPredA]), pb = uni(c.sflag[kPredB]);
+  const int e = tile_expert(p, a, b, pa, pb);
+  if (c.tid == 0) c.sflag[kStagedExpert] = e;
+  if (e < 0) return;
+  GemvDesc g;
+  desc_moe_upgate(p, l, a, c.wave, pa, pb, g);
+  const GenMap m{g};
+  const int nseg = (g.K + 511) >> 9;
+  const int n = min(2 * wave_rows(b - a, c.wave) * nseg, p.pre_units);
+  __attribute__((address_space(3))) char* dst = (__attribute__((address_space(3))) char*)pre_area_b(c);
+  int k = 0, seg = 0;
+  for (int u = 0; u < n; ++u) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(m.row(k), (uint32_t)g.K * 2u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + u * 1024, 16, c.lane * 16, seg * 1024, 0, kNT);
+    if (++seg == nseg) {
+      seg = 0;
+      ++k;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
 
 __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int index) {
   CKParams& p = c.p;
@@ -1665,17 +1832,26 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
   }
   __syncthreads();
   const int ea = uni(c.sflag[3]), eb = uni(c.sflag[4]);
-  // expert-rows r < F are expert a's rows, r >= F expert b's row r - F;
-  // streamed rows alternate gate and up
+  // The rows the instruction before this one staged are used only when they
+  // are the routed expert's (the router decides; the prediction only moved
+  // some loads earlier).
+  int staged = 0;
+  if (p.pre_units > 0 && c.instr > 0) {
+    const int se = uni(c.sflag[kStagedExpert]);
+    const bool hit = se >= 0 && se == tile_expert(p, a, b, ea, eb);
+    if (hit) staged = min(2 * wave_rows(b - a, c.wave) * ((p.d + 511) >> 9), p.pre_units);
+    if (c.tid == 0 && se >= 0) {
+      int* cnt = (int*)c.red;
+      cnt[kSpecHitWord] += hit ? 1 : 0;
+      cnt[kSpecNWord] += 1;
+    }
+  }
   GemvDesc g;
-  g.b00 = lptr(p, l, WL_EXPERTS + ea); g.b01 = lptr(p, l, WL_EXPERTS + eb); g.b02 = nullptr;
-  g.b10 = lptr(p, l, WL_EXPERTS + p.E + ea); g.b11 = lptr(p, l, WL_EXPERTS + p.E + eb); g.b12 = nullptr;
-  g.s1 = p.F; g.s2 = kNoSplit; g.K = p.d; g.R = 2; g.xoff1 = 0; g.a = a; g.w = c.wave;
+  desc_moe_upgate(p, l, a, c.wave, ea, eb, g);
   const GenMap m{g};
-  RowStream<GenMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane);
+  RowStream<GenMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, staged);
   rs.prefetch();
-  rs.run(c.xs, c.out);
-  mark_computed(c);
+  rs.run(c.xs, c.out, pre_area_b(c));
   __syncthreads();
   for (int i = c.tid; i < b - a; i += kThreads)
     ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
@@ -1716,7 +1892,6 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
   RowStream<GenMap> rs(m, p.F, 2 * wave_rows(b - a, c.wave), c.lane);
   rs.prefetch();
   rs.run(c.xs, c.out);
-  mark_computed(c);
   __syncthreads();
   const uint32_t otag = tag_of(p, c.t, l + 1);
   for (int i = c.tid; i < b - a; i += kThreads)
@@ -1809,7 +1984,16 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   const Fetch f[3] = {{qkv + q0 * HD, G * HD, tag, qs},
                       {qkv + p.qd + kvh * HD, HD, tag, ks},
                       {qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
-  if (!gather_inputs<3>(c, f)) return false;
+  // the producers of exactly these words, without the QKV stage's flags
+  // (G * HD + 2 HD <= 768 words: one load per thread)
+  {
+    bool ok = ll_poll<1>(c, f[0].src, f[0].n, f[0].tag, f[0].dst);
+    ok = ok && ll_poll<1>(c, f[1].src, f[1].n, f[1].tag, f[1].dst);
+    ok = ok && ll_poll<1>(c, f[2].src, f[2].n, f[2].tag, f[2].dst);
+    (void)ok;   // a stopping wavefront has set the abort word in LDS
+    if (!sync_ok(c)) return false;
+    mark_ready(c);
+  }
 
   // RoPE (pairs i, i + HD/2) on q heads and k; q pre-scaled for exp2 softmax
   const float qscale = 1.4426950408889634f / sqrtf((float)HD);
@@ -2065,8 +2249,14 @@ __device__ __forceinline__ bool op_areduce(Ctx& c, int l, int qh) {
   CKParams& p = c.p;
   const int HD = p.hd, n = p.n_chunks, W = HD + 2;
   const uint32_t tag = tag_of(p, c.t, l);
-  const Fetch f[1] = {{p.part + (size_t)c.seq * p.s_part + (size_t)qh * n * W, n * W, tag, c.xs}};
-  if (!gather_inputs<1>(c, f)) return false;
+  // this head's chunk partials, without the attention stage's flags
+  // (n * (HD + 2) <= 64 * 130 words: at most 9 loads per thread)
+  {
+    const bool ok = ll_poll<9>(c, p.part + (size_t)c.seq * p.s_part + (size_t)qh * n * W, n * W, tag, c.xs);
+    (void)ok;
+    if (!sync_ok(c)) return false;
+    mark_ready(c);
+  }
   float* const wk = c.red + 128;   // [64] chunk weights, then [4][HD <= 128] quarter sums below
   if (c.wave == 0) {
     const float m = c.lane < n ? c.xs[c.lane * W] : -INFINITY;
@@ -2119,11 +2309,25 @@ __device__ __forceinline__ void megakernel_body() {
     sflag[0] = 0;
     sflag[1] = 0;
     sflag[2] = -1;
+    sflag[kStagedExpert] = -1;
+    ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecHitWord] = 0;
+    ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecNWord] = 0;
   }
   __syncthreads();
   const int n = ldc_i32(pk->sched + kWords + wg);
   bool ok = true;
   for (int t = 0; t < pk->n_steps && ok; ++t) {
+    // Workgroup 0 reads the stop word once per step, between its last
+    // instruction of the previous step and the wait for this step's inputs
+    // (which the other workgroups' last tiles keep open): waits that end
+    // sooner than the pollers' stop checks cannot hide a stop request.  Once
+    // it stops publishing, every other workgroup ends up waiting on it long
+    // enough to see the abort word.
+    if (wg == 0 && __hip_atomic_load(pk->stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
+      if (threadIdx.x == 0) raise_at(pk->status, sflag, MKD_E_ABORTED, true, wg, 0, t);
+      ok = false;
+      break;
+    }
     for (int i = 0; i < n && ok; ++i) {
       // Opaque copies of the parameter pointer and thread id: nothing that
       // depends on them is hoisted out of the persistent loop, so values one
@@ -2144,14 +2348,17 @@ __device__ __forceinline__ void megakernel_body() {
             ldc_i32(ins + I_STAGE), index, ldc_i32(ins + I_WAIT_STAGE), ldc_i32(ins + I_WAIT_COUNT),
             ldc_i32(ins + I_WAIT_PREV), tr, BATCHED ? ldc_i32(ins + I_SEQ) : 0, BATCHED ? p.B : 1};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
-      // Dense gate/up weights are staged in LDS by the instruction before
-      // them: at the start of an O-projection (whose wait spans the whole
+      // The first weight units of the next gate/up instruction (dense: its
+      // first rows; MoE: the predicted expert's) are staged in LDS by this
+      // one: at the start of an O-projection (whose wait spans the whole
       // attention phase), else at the end of the instruction, once its own
       // loads are done.
       const int32_t* nx = i + 1 < n ? ins + kWords : nullptr;
-      const bool stage = p.pre_units > 0 && nx && ldc_i32(nx + I_OP) == OP_UPGATE;
+      const int nxop = nx ? ldc_i32(nx + I_OP) : OP_NOP;
+      const bool stage = p.pre_units > 0 && nxop == (MOE ? OP_MOE_UPGATE : OP_UPGATE);
       if (stage && op == OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+        else if constexpr (MOE) stage_predicted(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
         else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
       }
       switch (op) {
@@ -2171,10 +2378,23 @@ __device__ __forceinline__ void megakernel_body() {
         default: break;
       }
       if (ok) signal_done(c);
+      if constexpr (MOE) {
+        // the expert prediction of this layer, while xs still holds its input residual
+        if (ok && op == OP_QKV && p.pre_units > 0) predict_experts(c, l);
+      }
       if (ok && stage && op != OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
+        else if constexpr (MOE) stage_predicted(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
         else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
       }
+    }
+  }
+  if constexpr (MOE) {
+    // this workgroup's expert-prediction counts, summed over workgroups
+    if (pk->pre_units > 0 && threadIdx.x == 0) {
+      const int* cnt = (const int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats);
+      atomicAdd(pk->status + S_SPEC_HIT, cnt[kSpecHitWord]);
+      atomicAdd(pk->status + S_SPEC_N, cnt[kSpecNWord]);
     }
   }
   // the last step's argmax

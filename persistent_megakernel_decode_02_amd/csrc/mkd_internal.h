@@ -66,7 +66,9 @@ constexpr int WL_ROUTER = 6, WL_EXPERTS = 7;                // MoE: gate[E], up[
 inline int layer_slots(const mkd_config* c) { return c->n_experts ? 7 + 3 * c->n_experts : 9; }
 
 // status words (device)
-enum : int { S_CODE = 0, S_WG, S_INSTR, S_TOKEN, S_ABORT, S_WORDS = 8 };
+// S_SPEC_HIT / S_SPEC_N: MoE gate/up instructions whose routed expert had been
+// predicted (and its first rows staged), out of those that had a prediction
+enum : int { S_CODE = 0, S_WG, S_INSTR, S_TOKEN, S_ABORT, S_SPEC_HIT, S_SPEC_N, S_WORDS = 8 };
 
 struct KParams {
   const int32_t* sched;      // schedule words
@@ -107,11 +109,12 @@ struct KParams {
   int32_t x_floats;          // LDS floats reserved for the staged input vector
   int32_t out_floats;        // LDS floats for one instruction's GEMV row results
   int32_t res_floats;        // LDS floats for the residual rows of a tile (all sequences)
-  int32_t pre_units;         // dense gate/up: 1 KiB weight units per wavefront staged in LDS
-                             // by the instruction before it (0 = none)
+  int32_t pre_units;         // 1 KiB weight units per wavefront staged in LDS by the
+                             // instruction before their own (0 = none): dense gate/up rows,
+                             // or for MoE the predicted expert's first gate/up rows
   int32_t pre_off;           // where those units sit: 0 = their own area after the reduction
                              // scratch; else this many floats into the input area, past the
-                             // gate/up and O-projection inputs (several sequences)
+                             // gate/up and O-projection inputs (several sequences, MoE)
   float eps;
 };
 

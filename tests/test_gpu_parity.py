@@ -140,3 +140,66 @@ def test_tiny_random_launch_shapes(name, n_wg, n_chunks, T0):
     check_run(f"{name} n_wg={n_wg}", toks, logits, otoks, ologits)
     ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
     assert ok, f"appended kv max err {mx}"
+
+
+# Shapes the library accepts beyond the presets: one q head per kv head (G = 1,
+# attention instructions per head with and without split-KV), and MoE models
+# with 4 experts (router rows requested before the input wait, as for 8) and
+# 16 experts (more experts than wavefronts: the router is scored row by row).
+EXTRA_SHAPES = {
+    "tiny_g1": synth.ModelConfig("tiny-g1", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=4,
+                                 head_dim=64, d_ff=768, vocab=1024, rope_theta=10000.0),
+    "tiny_moe_e4": synth.ModelConfig("tiny-moe-e4", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                     head_dim=64, d_ff=512, vocab=1024, n_experts=4, top_k=2, rope_theta=1e6),
+    "tiny_moe_e16": synth.ModelConfig("tiny-moe-e16", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                      head_dim=128, d_ff=512, vocab=1024, n_experts=16, top_k=2, rope_theta=1e6),
+}
+
+
+@pytest.mark.parametrize("name,n_wg,n_chunks", [("tiny_g1", 256, 1), ("tiny_g1", 40, 3), ("tiny_moe_e4", 256, 1),
+                                                ("tiny_moe_e4", 33, 2), ("tiny_moe_e16", 256, 1),
+                                                ("tiny_moe_e16", 64, 4)])
+def test_accepted_shapes_beyond_the_presets(name, n_wg, n_chunks):
+    cfg = EXTRA_SHAPES[name]
+    T0, N = 50, 8
+    w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
+    say(f"{name} n_wg={n_wg} n_chunks={n_chunks}")
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=n_chunks)
+    first = synth.gen_tokens(1, cfg.vocab, stream=6)[0]
+    toks, logits = dec.decode(first, T0, N)
+    toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    dec.close()
+    w_cpu = synth.gen_weights(cfg, device="cpu", gain_std=0.1)
+    otoks, ologits, kv_o = oracle_run(cfg, w_cpu, synth.gen_kv_cache(cfg, T0 + N, T0), first, T0, N)
+    check_run(name, toks, logits, otoks, ologits)
+    ok, mx, _ = close_enough(kv_new, kv_o[:, :, :, T0:T0 + N])
+    assert ok, f"appended kv max err {mx}"
+
+
+@pytest.mark.parametrize("name,n_wg", [("tiny_moe", 256), ("tiny_moe", 33), ("tiny_moe_e4", 64)])
+def test_moe_expert_prediction_never_changes_the_result(name, n_wg):
+    """MoE models predict each layer's experts from the pre-attention residual
+    and stage the predicted expert's first gate/up rows early; the routed
+    expert is always the router's.  Launches with the prediction on and off
+    (staged units limited to 0) must be bit-identical, and the prediction
+    counts must cover every gate/up tile that lies in one expert's half."""
+    cfg = synth.PRESETS.get(name) or EXTRA_SHAPES[name]
+    T0, N = 40, 12
+    w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
+    kv0 = kv_gpu.clone()
+    first = synth.gen_tokens(1, cfg.vocab, stream=8)[0]
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1)
+    t_on, l_on = dec.decode(first, T0, N)
+    hits, preds = capi.mkd_spec_stats(dec.handle)
+    dec.close()
+    kv_on = kv_gpu.clone()
+    kv_gpu.copy_(kv0)
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1, lds_limits=(0, 0))
+    t_off, l_off = dec.decode(first, T0, N)
+    assert capi.mkd_spec_stats(dec.handle) == (0, 0)
+    dec.close()
+    say(f"{name} n_wg={n_wg}: {hits} of {preds} predictions named the routed expert")
+    assert preds > 0
+    assert torch.equal(t_on, t_off) and torch.equal(l_on, l_off), "prediction changed the result"
+    assert torch.equal(kv_on, kv_gpu)
