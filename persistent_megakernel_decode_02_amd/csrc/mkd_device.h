@@ -91,10 +91,6 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
-  return __hip_atomic_load((GLOBAL const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // LDS words shared by the workgroup's wavefronts.  The explicit address
 // space matters: a volatile access through a generic pointer becomes a flat
 // load, which also counts against the vector-memory counter, so the wait for
@@ -279,18 +275,27 @@ __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, cons
     }
   }
   if (!pending) return;
-  // some producer's store is still in flight: poll those words
+  // some producer's store is still in flight: re-read the pairs that hold
+  // such words, all of them in one round trip, until every word is current
   const uint64_t t0 = wall_clock64();
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(sp.w0, (uint32_t)sp.npairs * 16u);
   for (int it = 0; pending; ++it) {
     __builtin_amdgcn_s_sleep(1);
-    for (int b = 0; b < 2 * S; ++b) {
-      if (pending & (1u << b)) {
-        const int wi = 2 * (base + (b >> 1) * kThreads + c.tid) + (b & 1);  // word of the span
-        const uint64_t w = ll_load(sp.w0 + wi);
-        if ((uint32_t)(w >> 32) == tag) {
-          dst[m(wi - sp.lead)] = __uint_as_float((uint32_t)w);
-          pending &= ~(1u << b);
-        }
+    u32x4 v[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      if ((pending >> (2 * k)) & 3u)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (base + k * kThreads + c.tid) * 16, 0, kSC1);
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int i0 = 2 * (base + k * kThreads + c.tid) - sp.lead;
+      if ((pending & (1u << (2 * k))) && v[k].y == tag) {
+        dst[m(i0)] = __uint_as_float(v[k].x);
+        pending &= ~(1u << (2 * k));
+      }
+      if ((pending & (2u << (2 * k))) && v[k].w == tag) {
+        dst[m(i0 + 1)] = __uint_as_float(v[k].z);
+        pending &= ~(2u << (2 * k));
       }
     }
     if (pending && (it & 15) == 15) {
@@ -339,13 +344,14 @@ __device__ __forceinline__ bool sync_ok(Ctx& c) {
 }
 
 // Wait until all `count` instructions of `stage` have published step
-// `step_plus1 - 1` (their completion flags hold step + 1).  Wavefront 0 reads
-// the stage's flags -- one word per producer, so a single wide load covers
-// 256 producers -- and repeats with a short sleep until every flag is there.
+// `step_plus1 - 1` (their completion flags hold step + 1), or with slack > 0
+// until at most `slack` lanes still see a missing flag (4 flags per lane).
+// Wavefront 0 reads the stage's flags -- one word per producer, so a single
+// wide load covers 256 producers -- and repeats with a short sleep.
 // Producers only store their own flag (no read-modify-write on a shared
 // word, which would serialise 256 workgroups at one address).  False when
 // the launch is being aborted.
-__device__ __forceinline__ bool wait_counter(Ctx& c, int stage, uint32_t step_plus1, int count) {
+__device__ __forceinline__ bool wait_counter(Ctx& c, int stage, uint32_t step_plus1, int count, int slack = 0) {
   CKParams& p = c.p;
   if (c.wave == 0 && step_plus1 > 0) {
     const uint32_t* f = p.flags + (size_t)stage * p.flag_stride;
@@ -359,7 +365,7 @@ __device__ __forceinline__ bool wait_counter(Ctx& c, int stage, uint32_t step_pl
         mine = mine && (j + 0 >= count || v.x >= step_plus1) && (j + 1 >= count || v.y >= step_plus1) &&
                (j + 2 >= count || v.z >= step_plus1) && (j + 3 >= count || v.w >= step_plus1);
       }
-      if (__builtin_amdgcn_ballot_w64(!mine) == 0) break;
+      if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(!mine)) <= slack) break;
       __builtin_amdgcn_s_sleep(2);
       if ((it & 31) == 31) {
         int stop = 0;
@@ -426,21 +432,24 @@ struct Fetch {
   float* dst;
 };
 
-// Stage an instruction's inputs: wait on the producing stage's counter (one
-// word, polled by one thread), then read every word once, spinning per word
-// on any whose store is still in flight.  Reading the vectors before the
-// counter completes would mostly read them twice: in this schedule a
-// workgroup nearly always reaches a stage before its producers finish.
+// Stage an instruction's inputs: wait on the producing stage's flags until
+// at most kGatherSlack lanes' worth of producers (4 each) are outstanding,
+// then read every word once and re-read, in one round trip per round, those
+// whose store is still in flight (the tag tells).  The last producers' words
+// are thus caught as soon as they land, instead of a round trip after their
+// flags; reading while most producers are still busy would mostly re-read,
+// and 256 workgroups re-reading one vector load the lines that hold it.
 // The first batch of up to three fetches is issued before any is checked, so
 // one round trip covers an instruction's inputs (8192 words of the first,
 // 2048 of the others); longer inputs take further batches.
 // (the first fetch's words land in its destination through m; S0 16-byte
 // loads per thread per batch of it)
+constexpr int kGatherSlack = 16;
 template <int K, class M = InPlace, int S0 = 8>
 __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count,
                                        M m = M()) {
   constexpr int S1 = 2;
-  if (!wait_counter(c, stage, step_plus1, count)) return false;
+  if (!wait_counter(c, stage, step_plus1, count, kGatherSlack)) return false;
   Staged<S0> st0;
   Staged<S1> st1, st2;
   const Span sp0 = span_of(f[0].src, f[0].n);
