@@ -18,7 +18,6 @@ the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,21 +29,12 @@ if ROOT not in sys.path:
 
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "batch-1 decode tokens/s and % of HBM roofline (weight+KV bytes/token)"
-CSRC = os.path.join(ROOT, "persistent_megakernel_decode_02_amd", "csrc")
-# the device code of the kernels: a profile taken on other sources is stale
-KERNEL_SRCS = ["mkd_device.h", "mkd_internal.h", "mkd_kernel_dense.hip", "mkd_kernel_moe.hip",
-               "mkd_kernel_batch.hip", "mkd_launch.hip"]
+# digest of the kernels' device sources: a profile taken on other sources is stale
+from persistent_megakernel_decode_02_amd.profile_summary import kernel_digest  # noqa: E402
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
-
-
-def kernel_digest() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SRCS:
-        h.update(open(os.path.join(CSRC, name), "rb").read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload_key: str):

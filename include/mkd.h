@@ -313,10 +313,13 @@ int mkd_decode_batch(mkd_model* m, const int32_t* first_tokens, const int32_t* s
 int mkd_wait(mkd_model* m, int32_t timeout_ms, mkd_status* out);
 
 /* Ask the handle's running launch to stop: sets the stop word (word 0 of the
- * host control block) that every device-side wait polls; the launch then
- * ends with MKD_E_ABORTED (Hyperkernel teardown, "Hardware fault detection
- * and replanning": a stop word in the kernel's control block).  No effect
- * when no launch is in flight.  mkd_wait and the next launch clear it. */
+ * host control block).  Workgroup 0 reads it once per decode step; seeing it,
+ * it raises the device abort word, which every device-side wait polls, and
+ * the launch ends with MKD_E_ABORTED within about one step (Hyperkernel
+ * teardown, "Hardware fault detection and replanning": a stop word in the
+ * kernel's control block).
+ * No effect when no launch is in flight.  mkd_wait and the next launch
+ * clear it. */
 int mkd_abort(mkd_model* m);
 
 /* Device-side deadline, in milliseconds, for any single wait of a workgroup

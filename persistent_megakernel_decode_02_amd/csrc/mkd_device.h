@@ -176,7 +176,7 @@ struct Ctx {
   float* red;    // reduction scratch     [kRed]
   lds_vint* sflag;  // LDS ints: [0] abort, [1] token, [2] token step, [3..6] route
   int wg, instr, t, tid, lane, wave;
-  int stage, index, wait_stage, wait_count, wait_prev;  // from the instruction words
+  int stage, index;                              // from the instruction words
   uint64_t* tr;                                  // this instruction's trace entry, or null
   int seq;                                       // sequence of a per-sequence instruction
   int B;                                         // sequences decoded together (a constant 1
@@ -298,14 +298,14 @@ __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, cons
         pending &= ~(2u << (2 * k));
       }
     }
+    // (the stop word lives in host memory: a read of it crosses PCIe, and
+    // every wavefront of the chip re-reading it here queued those reads for
+    // hundreds of microseconds; a stop reaches these loops as the abort word,
+    // which the flag waits and workgroup 0's per-step read set)
     if (pending && (it & 15) == 15) {
       if (c.sflag[0] ||
           __hip_atomic_load(&c.p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
         c.sflag[0] = 1;
-        break;
-      }
-      if (__hip_atomic_load(c.p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
-        raise_error(c, MKD_E_ABORTED, true);
         break;
       }
       if (wall_clock64() - t0 > c.p.watchdog_ticks) {
@@ -343,61 +343,11 @@ __device__ __forceinline__ bool sync_ok(Ctx& c) {
   return uni(c.sflag[0]) == 0;
 }
 
-// Wait until all `count` instructions of `stage` have published step
-// `step_plus1 - 1` (their completion flags hold step + 1), or with slack > 0
-// until at most `slack` lanes still see a missing flag (4 flags per lane).
-// Wavefront 0 reads the stage's flags -- one word per producer, so a single
-// wide load covers 256 producers -- and repeats with a short sleep.
-// Producers only store their own flag (no read-modify-write on a shared
-// word, which would serialise 256 workgroups at one address).  False when
-// the launch is being aborted.
-__device__ __forceinline__ bool wait_counter(Ctx& c, int stage, uint32_t step_plus1, int count, int slack = 0) {
-  CKParams& p = c.p;
-  if (c.wave == 0 && step_plus1 > 0) {
-    const uint32_t* f = p.flags + (size_t)stage * p.flag_stride;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(f, (uint32_t)count * 4u);
-    const uint64_t t0 = wall_clock64();
-    for (int it = 0;; ++it) {
-      bool mine = true;
-      for (int base = 0; base < count; base += 256) {
-        const int j = base + c.lane * 4;
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, c.lane * 16, base * 4, kSC1);
-        mine = mine && (j + 0 >= count || v.x >= step_plus1) && (j + 1 >= count || v.y >= step_plus1) &&
-               (j + 2 >= count || v.z >= step_plus1) && (j + 3 >= count || v.w >= step_plus1);
-      }
-      if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(!mine)) <= slack) break;
-      __builtin_amdgcn_s_sleep(2);
-      if ((it & 31) == 31) {
-        int stop = 0;
-        if (__hip_atomic_load(&p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          stop = 1;
-        } else if (__hip_atomic_load(p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
-          stop = 2;
-        } else if (wall_clock64() - t0 > p.watchdog_ticks) {
-          stop = 3;
-        }
-        stop = uni(stop);
-        if (stop) {
-          if (c.lane == 0) {
-            if (stop == 1) c.sflag[0] = 1;
-            else raise_error(c, stop == 2 ? MKD_E_ABORTED : MKD_E_WATCHDOG, true);
-          }
-          break;
-        }
-      }
-    }
-  }
-  return sync_ok(c);
-}
-
-// the wait this instruction's schedule words name
-__device__ __forceinline__ bool wait_inputs(Ctx& c) {
-  return wait_counter(c, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count);
-}
-
-// Mark this instruction done for this step.  Called after every thread has
-// issued its output stores; the flag may become visible before those stores
-// do, which is harmless: consumers still check each word's tag.
+// Mark this instruction done for this step: a barrier (the next instruction
+// reuses the LDS areas the epilogue read) and the instruction's completion
+// flag, step + 1.  No consumer waits on the flags -- inputs are recognised by
+// their tags -- they are the launch's progress record: after an abort or a
+// watchdog error they show how far each instruction got.
 __device__ __forceinline__ void signal_done(Ctx& c) {
   __syncthreads();
   if (c.tid == 0) {
@@ -432,24 +382,21 @@ struct Fetch {
   float* dst;
 };
 
-// Stage an instruction's inputs: wait on the producing stage's flags until
-// at most kGatherSlack lanes' worth of producers (4 each) are outstanding,
-// then read every word once and re-read, in one round trip per round, those
-// whose store is still in flight (the tag tells).  The last producers' words
-// are thus caught as soon as they land, instead of a round trip after their
-// flags; reading while most producers are still busy would mostly re-read,
-// and 256 workgroups re-reading one vector load the lines that hold it.
+// Stage an instruction's inputs, with no wait on the producers' flags: every
+// thread reads its share of the words at once and re-reads, one round trip
+// per round, the pairs whose tag is still old until every word is current.
+// Each word is caught as soon as its producer's store lands, instead of a
+// round trip after the producing stage's last flag.  (A flag wait first, or
+// until at most 64 producers were left, measured slower; re-reading the host
+// stop word in these loops is what once made this scheme erratic.)
 // The first batch of up to three fetches is issued before any is checked, so
 // one round trip covers an instruction's inputs (8192 words of the first,
 // 2048 of the others); longer inputs take further batches.
 // (the first fetch's words land in its destination through m; S0 16-byte
 // loads per thread per batch of it)
-constexpr int kGatherSlack = 16;
 template <int K, class M = InPlace, int S0 = 8>
-__device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, uint32_t step_plus1, int count,
-                                       M m = M()) {
+__device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], M m = M()) {
   constexpr int S1 = 2;
-  if (!wait_counter(c, stage, step_plus1, count, kGatherSlack)) return false;
   Staged<S0> st0;
   Staged<S1> st1, st2;
   const Span sp0 = span_of(f[0].src, f[0].n);
@@ -478,7 +425,7 @@ __device__ __forceinline__ bool gather(Ctx& c, const Fetch (&f)[K], int stage, u
 
 template <int K, class M = InPlace, int S0 = 8>
 __device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K], M m = M()) {
-  return gather<K, M, S0>(c, f, c.wait_stage, (uint32_t)(c.wait_prev ? c.t : c.t + 1), c.wait_count, m);
+  return gather<K, M, S0>(c, f, m);
 }
 
 // Stage small inputs without waiting for the producing stage's flags: every
@@ -489,8 +436,8 @@ __device__ __forceinline__ bool gather_inputs(Ctx& c, const Fetch (&f)[K], M m =
 // v rows, a split-KV reduction for its head's chunk partials -- and saves the
 // round trip of the flag poll.  Only for inputs of at most kThreads * S word
 // pairs read by few instructions: the reads repeat until the data is there.
-// The abort word, stop word and deadline are looked at every 32 rounds, by
-// each wavefront as a whole.
+// The abort word and the deadline are looked at every 32 rounds, by each
+// wavefront as a whole (a stop request arrives as the abort word).
 template <int S>
 __device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
   CKParams& p = c.p;
@@ -524,8 +471,6 @@ __device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint
       int stop = 0;
       if (c.sflag[0] || __hip_atomic_load(&p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
         stop = 1;
-      } else if (__hip_atomic_load(p.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
-        stop = 2;
       } else if (wall_clock64() - t0 > p.watchdog_ticks) {
         stop = 3;
       }
@@ -533,7 +478,7 @@ __device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint
       if (stop) {
         if (c.lane == 0) {
           if (stop == 1) c.sflag[0] = 1;
-          else raise_error(c, stop == 2 ? MKD_E_ABORTED : MKD_E_WATCHDOG, true);
+          else raise_error(c, MKD_E_WATCHDOG, true);
         }
         return false;
       }
@@ -610,12 +555,12 @@ __device__ __forceinline__ int argmax_staged(Ctx& c, int sq) {
   return uni(bi);
 }
 
-// every sequence's LM-head tile partials of step tt, staged in LDS at xs;
-// waits for the LM-head stage first
+// every sequence's LM-head tile partials of step tt, staged in LDS at xs
+// (re-read until every tile's pair is current)
 __device__ __forceinline__ bool fetch_partials(Ctx& c, int tt) {
   CKParams& p = c.p;
   const Fetch f[1] = {{p.lm, 2 * p.n_lm_tiles * c.B, tag_of(p, tt, p.L), c.xs}};
-  return gather<1>(c, f, p.n_stages - 1, (uint32_t)(tt + 1), p.n_lm_tiles);
+  return gather<1>(c, f);
 }
 
 // Every sequence's token of step sflag[2], kept at the end of the reduction
@@ -2354,8 +2299,7 @@ __device__ __forceinline__ void megakernel_body() {
       Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.res_floats,
             smem + p.x_floats + p.res_floats + p.out_floats,
             sflag, wg, i, t, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6),
-            ldc_i32(ins + I_STAGE), index, ldc_i32(ins + I_WAIT_STAGE), ldc_i32(ins + I_WAIT_COUNT),
-            ldc_i32(ins + I_WAIT_PREV), tr, BATCHED ? ldc_i32(ins + I_SEQ) : 0, BATCHED ? p.B : 1};
+            ldc_i32(ins + I_STAGE), index, tr, BATCHED ? ldc_i32(ins + I_SEQ) : 0, BATCHED ? p.B : 1};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
       // The first weight units of the next gate/up instruction (dense: its
       // first rows; MoE: the predicted expert's) are staged in LDS by this
@@ -2412,8 +2356,8 @@ __device__ __forceinline__ void megakernel_body() {
     const int tid = threadIdx.x;
     Ctx c{p, smem, smem + p.x_floats, smem + p.x_floats + p.res_floats,
           smem + p.x_floats + p.res_floats + p.out_floats,
-          sflag, wg, 0, p.n_steps, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6), 0, 0, 0, 0,
-          0, nullptr, 0, BATCHED ? p.B : 1};
+          sflag, wg, 0, p.n_steps, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6), 0, 0,
+          nullptr, 0, BATCHED ? p.B : 1};
     if (fetch_partials(c, p.n_steps - 1)) {
       for (int b = 0; b < c.B; ++b) {
         const int am = argmax_staged(c, b);
