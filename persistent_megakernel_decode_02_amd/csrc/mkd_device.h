@@ -486,6 +486,62 @@ __device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint
   }
 }
 
+// As ll_poll, for K inputs of at most kThreads word pairs each, polled
+// together: per round, one 16-byte load per thread and input, issued only
+// while that pair still holds an old word, so one round trip covers all K.
+template <int K>
+__device__ __forceinline__ bool ll_poll_k(Ctx& c, const Fetch (&f)[K]) {
+  CKParams& p = c.p;
+  Span sp[K];
+  unsigned pending = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    sp[k] = span_of(f[k].src, f[k].n);
+    const int i0 = 2 * c.tid - sp[k].lead;
+    if (i0 >= 0 && i0 < f[k].n) pending |= 1u << (2 * k);
+    if (i0 + 1 >= 0 && i0 + 1 < f[k].n) pending |= 2u << (2 * k);
+  }
+  const uint64_t t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+    u32x4 v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((pending >> (2 * k)) & 3u)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(sp[k].w0, (uint32_t)sp[k].npairs * 16u),
+                                                     c.tid * 16, 0, kSC1);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i0 = 2 * c.tid - sp[k].lead;
+      if ((pending & (1u << (2 * k))) && v[k].y == f[k].tag) {
+        f[k].dst[i0] = __uint_as_float(v[k].x);
+        pending &= ~(1u << (2 * k));
+      }
+      if ((pending & (2u << (2 * k))) && v[k].w == f[k].tag) {
+        f[k].dst[i0 + 1] = __uint_as_float(v[k].z);
+        pending &= ~(2u << (2 * k));
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pending != 0) == 0) return true;   // this wavefront's words are in
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 31) == 31) {
+      int stop = 0;
+      if (c.sflag[0] || __hip_atomic_load(&p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        stop = 1;
+      } else if (wall_clock64() - t0 > p.watchdog_ticks) {
+        stop = 3;
+      }
+      stop = uni(stop);
+      if (stop) {
+        if (c.lane == 0) {
+          if (stop == 1) c.sflag[0] = 1;
+          else raise_error(c, MKD_E_WATCHDOG, true);
+        }
+        return false;
+      }
+    }
+  }
+}
+
 // RMSNorm gains of this thread's elements (i = tid + k * kThreads), read
 // before the inputs are waited for; covers d <= kGainRegs * kThreads
 constexpr int kGainRegs = 8;
@@ -1938,12 +1994,10 @@ __device__ __forceinline__ bool op_attn_t(Ctx& c, int l, int kvh, int chunk, int
   const Fetch f[3] = {{qkv + q0 * HD, G * HD, tag, qs},
                       {qkv + p.qd + kvh * HD, HD, tag, ks},
                       {qkv + p.qd + p.kvd + kvh * HD, HD, tag, vs}};
-  // the producers of exactly these words, without the QKV stage's flags
-  // (G * HD + 2 HD <= 768 words: one load per thread)
+  // the producers of exactly these words, all three polled together
+  // (G * HD <= 512 and HD <= 128 words: one load per thread and input)
   {
-    bool ok = ll_poll<1>(c, f[0].src, f[0].n, f[0].tag, f[0].dst);
-    ok = ok && ll_poll<1>(c, f[1].src, f[1].n, f[1].tag, f[1].dst);
-    ok = ok && ll_poll<1>(c, f[2].src, f[2].n, f[2].tag, f[2].dst);
+    const bool ok = ll_poll_k<3>(c, f);
     (void)ok;   // a stopping wavefront has set the abort word in LDS
     if (!sync_ok(c)) return false;
     mark_ready(c);
