@@ -99,8 +99,8 @@ def write_kernel_trace(a) -> None:
     b = _bench(a.bench)
     lines = [f"# {a.kernel}, {a.workload}: rocprofv3 kernel trace", ""]
     lines.append("Commands (repo root, one MI355X; the profiled run dispatches the same grid without the "
-                 "cooperative flag, because rocprofv3 on this image crashes at process exit, before writing "
-                 "output, once a process made a cooperative dispatch):")
+                 "cooperative flag: after a cooperative dispatch, rocprofv3 7.2 crashes at process exit "
+                 "before it writes any output):")
     lines.append("")
     lines.append("```")
     lines += a.command
