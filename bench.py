@@ -132,6 +132,8 @@ def main() -> int:
                     help="cap on the weight units per wavefront staged ahead in LDS (-1: no cap; 0 turns "
                          "staging, and for MoE the expert prediction, off)")
     ap.add_argument("--calib-copy", type=int, default=0, help="only run a plain copy of this many bytes")
+    ap.add_argument("--read-probe-gib", type=float, default=4.0,
+                    help="size of the plain streaming read that measures the reachable HBM rate (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -218,6 +220,8 @@ def main() -> int:
     if args.trace:
         trace_breakdown(dec, one, N, args.trace_out, f"{args.workload} KV {T0}, {N} steps per launch")
 
+    probe = read_probe(args.read_probe_gib) if args.read_probe_gib > 0 else None
+
     cpu = None
     if args.cpu_seconds > 0 and B == 1:
         cpu = cpu_baseline(cfg, T0, args.cpu_seconds, first, w)
@@ -256,12 +260,41 @@ def main() -> int:
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": kernel,
                      "algorithmic_bytes_per_launch": n_bytes,
-                     "kernel_ms_mean": kernel_s * 1e3},
+                     "kernel_ms_mean": kernel_s * 1e3,
+                     "read_probe_gbs": probe},
         "cpu_baseline": cpu,
     }
     dec.close()
     print(json.dumps(out), flush=True)
     return 0
+
+
+def read_probe(gib: float):
+    """GB/s of a plain streaming read of a device buffer (the library's
+    mkd_read_probe; median of 5 timed launches after one untimed), measured
+    on torch's current stream with its events: the HBM read rate this device
+    reaches, beside which the decode kernels' fraction of the published peak
+    is read."""
+    import numpy as np
+    import torch
+    from persistent_megakernel_decode_02_amd import capi
+    n = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    capi.mkd_read_probe(buf, sink)
+    ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        capi.mkd_read_probe(buf, sink)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = n / (float(np.median(ms)) * 1e-3) / 1e9
+    log(f"read probe: {n / 2**30:.1f} GiB at {gbs:.0f} GB/s")
+    return gbs
 
 
 def stage_bytes(cfg, op: str, pos: int) -> int:

@@ -351,6 +351,19 @@ int mkd_kernel_ms(mkd_model* m, float* ms);
  * Plumbing. */
 int mkd_clock_hz(mkd_model* m, double* hz);
 
+/* A plain streaming read of `bytes` (a multiple of 16, at least 16) of
+ * device memory at buf_dev, enqueued on `stream` (a hipStream_t, NULL for
+ * the default stream) with 16-byte non-temporal loads spread over eight
+ * 256-thread workgroups per CU: the HBM read rate the device actually
+ * reaches, beside which the decode kernels' fraction of the published peak
+ * is read (Hyperkernel teardown, "Where the numbers sit against the
+ * hardware": the bytes a kernel must read over the bandwidth bound its time).
+ * sink_dev: one device uint32 the kernel may write (it does not in
+ * practice).  The caller times it (e.g. with events on the same stream).
+ * MKD_E_INVALID for null pointers, a bad size or a buffer not 16-byte
+ * aligned, MKD_E_HIP on a launch failure.  Asynchronous. */
+int mkd_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* stream);
+
 /* Speculative expert prediction of the last launch mkd_wait saw end (MoE
  * models; epic-kernel README, "Speculative expert prediction": the top-2
  * experts are predicted from the pre-attention residual before the router

@@ -32,7 +32,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-I" + 
 
 # device translation units (each kernel on its own, so they compile in
 # parallel) and host ones; every object depends on the headers too
-DEVICE_SRCS = ["mkd_kernel_dense.hip", "mkd_kernel_moe.hip", "mkd_kernel_batch.hip", "mkd_launch.hip"]
+DEVICE_SRCS = ["mkd_kernel_dense.hip", "mkd_kernel_moe.hip", "mkd_kernel_batch.hip", "mkd_launch.hip", "mkd_probe.hip"]
 HOST_SRCS = ["mkd_api.cpp", "schedule.cpp"]
 HEADERS = [os.path.join(CSRC, "mkd_device.h"), os.path.join(CSRC, "mkd_internal.h"),
            os.path.join(INCLUDE, "mkd.h")]

@@ -904,6 +904,24 @@ int mkd_set_lds_limits(mkd_model* m, int32_t max_input_floats, int32_t max_stage
   return MKD_OK;
 }
 
+}  // extern "C"
+
+namespace mkd {
+// csrc/mkd_probe.hip: a plain streaming read of buf (bytes, a multiple of 16) on `stream`
+int read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream, const char** why);
+}  // namespace mkd
+
+extern "C" {
+
+int mkd_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* stream) {
+  if (!buf_dev || !sink_dev) return fail(MKD_E_INVALID, "null buffer or sink");
+  if (bytes < 16 || bytes % 16) return fail(MKD_E_INVALID, "bytes must be a positive multiple of 16");
+  if ((uintptr_t)buf_dev % 16) return fail(MKD_E_INVALID, "the buffer must be 16-byte aligned");
+  const char* why = "";
+  const int rc = read_probe(buf_dev, bytes, sink_dev, stream, &why);
+  return rc == MKD_OK ? MKD_OK : fail(rc, why);
+}
+
 int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions) {
   if (!m || !hits || !predictions) return fail(MKD_E_INVALID, "null argument");
   *hits = m->spec_hit;

@@ -1,6 +1,7 @@
 """The C-ABI library on the host: it loads, exports every function the header
 declares, and its host logic (config checks, weight shapes, the schedule
 builder and validator) agrees with the oracle -- no GPU calls."""
+import ctypes
 import os
 import re
 
@@ -290,3 +291,14 @@ def test_validator_rejects_mutations():
             assert not lib_ok
         n_bad += not lib_ok
     assert n_bad > 150
+
+
+def test_read_probe_rejects_bad_arguments_before_any_device_call():
+    """The streaming-read probe checks its arguments on the host: null
+    pointers, a size that is not a positive multiple of 16, a misaligned
+    buffer."""
+    lib = capi.load()
+    assert lib.mkd_read_probe(None, 16, None, None) == capi.MKD_E_INVALID
+    assert lib.mkd_read_probe(ctypes.c_void_p(4096), 15, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID
+    assert lib.mkd_read_probe(ctypes.c_void_p(4096), 0, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID
+    assert lib.mkd_read_probe(ctypes.c_void_p(4104), 64, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID

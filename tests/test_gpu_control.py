@@ -119,3 +119,22 @@ def test_workspace_too_small_for_a_schedule_is_rejected():
     toks, _ = dec.decode(3, 32, 4, want_logits=False)
     assert toks.numel() == 4
     dec.close()
+
+
+def test_read_probe_runs_and_reads_the_whole_buffer():
+    """mkd_read_probe streams a device buffer; it writes its sink only if the
+    XOR of everything read equals a value a buffer of ones cannot give, so the
+    sink stays 0, and it runs at a plausible HBM rate."""
+    require_gpu()
+    buf = torch.ones(1 << 26, dtype=torch.int32, device="cuda")   # 256 MiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    capi.mkd_read_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    capi.mkd_read_probe(buf, sink)
+    e1.record()
+    e1.synchronize()
+    gbs = buf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    say(f"read probe: {gbs:.0f} GB/s over 256 MiB")
+    assert int(sink.item()) == 0
+    assert 500 < gbs < 20000
