@@ -258,9 +258,14 @@ struct SlicePad {
   __device__ __forceinline__ int operator()(int i) const { return i + (i / (8 * NB)) * 4; }
 };
 
+// A thread's words still to come are two bits per 16-byte load k of a batch
+// (bit 2k: the pair's first word, bit 2k + 1: its second) of a 32-bit mask,
+// so a batch has at most 16 loads per thread: a shift by 32 or more is
+// undefined, and the compiler may then drop words that are still pending.
 template <int S, class M = InPlace>
 __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, const Staged<S>& st, int n,
                                           uint32_t tag, float* dst, M m = M()) {
+  static_assert(S >= 1 && S <= 16, "two pending bits per load in a 32-bit mask");
   unsigned pending = 0;
 #pragma unroll
   for (int k = 0; k < S; ++k) {
@@ -301,7 +306,7 @@ __device__ __forceinline__ void ll_finish(Ctx& c, const Span& sp, int base, cons
     // (the stop word lives in host memory: a read of it crosses PCIe, and
     // every wavefront of the chip re-reading it here queued those reads for
     // hundreds of microseconds; a stop reaches these loops as the abort word,
-    // which the flag waits and workgroup 0's per-step read set)
+    // which workgroup 0 raises when its per-step read finds the stop word)
     if (pending && (it & 15) == 15) {
       if (c.sflag[0] ||
           __hip_atomic_load(&c.p.status[S_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -442,6 +447,7 @@ template <int S>
 __device__ __forceinline__ bool ll_poll(Ctx& c, const uint64_t* src, int n, uint32_t tag, float* dst) {
   CKParams& p = c.p;
   const Span sp = span_of(src, n);
+  static_assert(S >= 1 && S <= 16, "two pending bits per load in a 32-bit mask");
   unsigned pending = 0;
 #pragma unroll
   for (int k = 0; k < S; ++k) {
@@ -493,6 +499,7 @@ template <int K>
 __device__ __forceinline__ bool ll_poll_k(Ctx& c, const Fetch (&f)[K]) {
   CKParams& p = c.p;
   Span sp[K];
+  static_assert(K <= 16, "two pending bits per input in a 32-bit mask");
   unsigned pending = 0;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -1665,6 +1672,10 @@ __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b,
 // loaded early).  LDS words of the prediction and of its outcome counts.
 constexpr int kPredA = 5, kPredB = 6, kStagedExpert = 7;   // sflag words
 constexpr int kSpecHitWord = 252, kSpecNWord = 253;         // int words of the reduction scratch
+// The route of a layer (experts a and b as int bits, their weights) in words
+// kRouteWords .. + 3 of the reduction scratch, and at kRouteStamp the tag of
+// the step and layer it belongs to (0: none yet)
+constexpr int kRouteWords = 8, kRouteStamp = 12;
 
 // The expert whose gate/up rows the tile [a, b) of a layer's stacked
 // (expert a, expert b) rows reads, given the two experts; -1 if the tile
@@ -1833,12 +1844,16 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
     const float q = expf(zb - za);
     c.sflag[3] = ea;
     c.sflag[4] = eb;
-    if (index == 0) {
-      ll_store(p.route + 0, __int_as_float(ea), tag);
-      ll_store(p.route + 1, __int_as_float(eb), tag);
-      ll_store(p.route + 2, 1.0f / (1.0f + q), tag);
-      ll_store(p.route + 3, q / (1.0f + q), tag);
-    }
+    // the route stays in LDS for this workgroup's down-projection tile of
+    // the layer; the first gate/up tile publishes it for the others
+    float* rt = c.red + kRouteWords;
+    rt[0] = __int_as_float(ea);
+    rt[1] = __int_as_float(eb);
+    rt[2] = 1.0f / (1.0f + q);
+    rt[3] = q / (1.0f + q);
+    c.red[kRouteStamp] = __uint_as_float(tag);
+    if (index == 0)
+      for (int k = 0; k < 4; ++k) ll_store(p.route + k, rt[k], tag);
   }
   __syncthreads();
   const int ea = uni(c.sflag[3]), eb = uni(c.sflag[4]);
@@ -1872,23 +1887,29 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
   CKParams& p = c.p;
   const uint32_t tag = tag_of(p, c.t, l);
   const int Fpad = (p.F + 511) & ~511;
+  float* rt = c.red + kRouteWords;
+  // When this workgroup ran a gate/up tile of the layer, the route is already
+  // in LDS: the experts' rows are then requested before the activations are
+  // waited for (expert widths of whole 512-element segments; Mixtral-shaped
+  // decode 4590-4625 against 4635-4704 us/token).  Otherwise the route is
+  // fetched with the activations.
+  const bool own = (p.F & 511) == 0 && __float_as_uint(c.red[kRouteStamp]) == tag;
   if (p.F & 511) {
-    const Fetch f[4] = {{p.route, 4, tag, c.red + 8}, {p.act, p.F, tag, c.xs},
+    const Fetch f[4] = {{p.route, 4, tag, rt}, {p.act, p.F, tag, c.xs},
                         {p.act + p.F, p.F, tag, c.xs + Fpad}, {p.hmid + a, b - a, tag, c.res}};
     pad_zero(c, c.xs, p.F);
     pad_zero(c, c.xs + Fpad, p.F);
     if (!gather_inputs<4>(c, f)) return false;
-  } else {
+  } else if (!own) {
     // both experts' activations are one contiguous span, in the same layout
     // in LDS: one fetch, 16 loads per thread per round trip (two round trips
     // for Mixtral's 2 x 14336 words, against a dozen in 2048-word pieces)
-    const Fetch f[3] = {{p.act, 2 * p.F, tag, c.xs}, {p.hmid + a, b - a, tag, c.res},
-                        {p.route, 4, tag, c.red + 8}};
+    const Fetch f[3] = {{p.act, 2 * p.F, tag, c.xs}, {p.hmid + a, b - a, tag, c.res}, {p.route, 4, tag, rt}};
     if (!gather_inputs<3, InPlace, 16>(c, f)) return false;
   }
-  const int ea = uni(__float_as_int(c.red[8])), eb = uni(__float_as_int(c.red[9]));
-  const float wa = __int_as_float(uni(__float_as_int(c.red[10])));
-  const float wb = __int_as_float(uni(__float_as_int(c.red[11])));
+  const int ea = uni(__float_as_int(rt[0])), eb = uni(__float_as_int(rt[1]));
+  const float wa = __int_as_float(uni(__float_as_int(rt[2])));
+  const float wb = __int_as_float(uni(__float_as_int(rt[3])));
   if (ea < 0 || ea >= p.E || eb < 0 || eb >= p.E) {
     if (c.tid == 0) raise_error(c, MKD_E_BOUNDS, true);
     __syncthreads();
@@ -1901,6 +1922,11 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c, int l, int a, int b) {
   const GenMap m{g};
   RowStream<GenMap> rs(m, p.F, 2 * wave_rows(b - a, c.wave), c.lane);
   rs.prefetch();
+  if (own) {
+    // (the rows requested above are in flight meanwhile)
+    const Fetch f[2] = {{p.act, 2 * p.F, tag, c.xs}, {p.hmid + a, b - a, tag, c.res}};
+    if (!gather_inputs<2, InPlace, 16>(c, f)) return false;
+  }
   rs.run(c.xs, c.out);
   __syncthreads();
   const uint32_t otag = tag_of(p, c.t, l + 1);
@@ -2320,6 +2346,7 @@ __device__ __forceinline__ void megakernel_body() {
     sflag[kStagedExpert] = -1;
     ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecHitWord] = 0;
     ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecNWord] = 0;
+    if constexpr (MOE) ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kRouteStamp] = 0;
   }
   __syncthreads();
   const int n = ldc_i32(pk->sched + kWords + wg);

@@ -145,7 +145,8 @@ def test_tiny_random_launch_shapes(name, n_wg, n_chunks, T0):
 # Shapes the library accepts beyond the presets: one q head per kv head (G = 1,
 # attention instructions per head with and without split-KV), and MoE models
 # with 4 experts (router rows requested before the input wait, as for 8) and
-# 16 experts (more experts than wavefronts: the router is scored row by row).
+# 16 experts (more experts than wavefronts: the router is scored row by row),
+# and an expert width that is not a whole number of 512-element segments.
 EXTRA_SHAPES = {
     "tiny_g1": synth.ModelConfig("tiny-g1", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=4,
                                  head_dim=64, d_ff=768, vocab=1024, rope_theta=10000.0),
@@ -153,12 +154,17 @@ EXTRA_SHAPES = {
                                      head_dim=64, d_ff=512, vocab=1024, n_experts=4, top_k=2, rope_theta=1e6),
     "tiny_moe_e16": synth.ModelConfig("tiny-moe-e16", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
                                       head_dim=128, d_ff=512, vocab=1024, n_experts=16, top_k=2, rope_theta=1e6),
+    # an expert width that is not a multiple of 512: each expert's activations
+    # are fetched on their own, zero-padded to whole segments
+    "tiny_moe_f768": synth.ModelConfig("tiny-moe-f768", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
+                                       head_dim=64, d_ff=768, vocab=1024, n_experts=8, top_k=2, rope_theta=1e6),
 }
 
 
 @pytest.mark.parametrize("name,n_wg,n_chunks", [("tiny_g1", 256, 1), ("tiny_g1", 40, 3), ("tiny_moe_e4", 256, 1),
                                                 ("tiny_moe_e4", 33, 2), ("tiny_moe_e16", 256, 1),
-                                                ("tiny_moe_e16", 64, 4)])
+                                                ("tiny_moe_e16", 64, 4), ("tiny_moe_f768", 256, 1),
+                                                ("tiny_moe_f768", 33, 2)])
 def test_accepted_shapes_beyond_the_presets(name, n_wg, n_chunks):
     cfg = EXTRA_SHAPES[name]
     T0, N = 50, 8
