@@ -130,7 +130,10 @@ def main() -> int:
                     help="dispatch the grid without the cooperative flag (for profilers)")
     ap.add_argument("--staged-units", type=int, default=-1,
                     help="cap on the weight units per wavefront staged ahead in LDS (-1: no cap; 0 turns "
-                         "staging, and for MoE the expert prediction, off)")
+                         "staging off)")
+    ap.add_argument("--expert-prediction", action="store_true",
+                    help="MoE: predict each layer's experts and stage their first rows (off by default: "
+                         "measured slower on MI355X)")
     ap.add_argument("--calib-copy", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--read-probe-gib", type=float, default=4.0,
                     help="size of the plain streaming read that measures the reachable HBM rate (0: skip)")
@@ -182,7 +185,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"inputs generated in {time.perf_counter() - tg:.1f}s")
     dec = Decoder(cfg, w, kv, max_seq, n_wg=n_wg, n_chunks=n_chunks, batch=B, cooperative=not args.plain_launch,
-                  lds_limits=None if args.staged_units < 0 else (0, args.staged_units))
+                  lds_limits=None if args.staged_units < 0 else (0, args.staged_units),
+                  expert_prediction=args.expert_prediction)
     dec.trace_pos = T0
     log(f"schedule: n_wg={dec.n_wg} n_chunks={dec.n_chunks} max_instr={dec.max_instr} batch={B}")
     firsts = synth.gen_tokens(B, cfg.vocab)
@@ -229,8 +233,10 @@ def main() -> int:
     spec = None
     if cfg.is_moe:
         hits, preds = capi.mkd_spec_stats(dec.handle)
-        spec = {"hits": hits, "predictions": preds, "hit_rate": hits / preds if preds else None}
-        log(f"expert prediction: {hits} of {preds} gate/up tiles had their routed expert predicted")
+        spec = {"on": bool(args.expert_prediction), "hits": hits, "predictions": preds,
+                "hit_rate": hits / preds if preds else None}
+        log(f"expert prediction {'on' if args.expert_prediction else 'off'}: {hits} of {preds} gate/up tiles "
+            f"had their routed expert predicted")
     key = f"{args.workload}_kv{T0}_n{N}" + (f"_b{B}" if B > 1 else "")
     kernel = "mkd_megakernel_batch" if B > 1 else ("mkd_megakernel_moe" if cfg.is_moe else "mkd_megakernel")
     traffic = measured_traffic(kernel, key)

@@ -364,18 +364,28 @@ int mkd_clock_hz(mkd_model* m, double* hz);
  * aligned, MKD_E_HIP on a launch failure.  Asynchronous. */
 int mkd_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* stream);
 
-/* Speculative expert prediction of the last launch mkd_wait saw end (MoE
- * models; epic-kernel README, "Speculative expert prediction": the top-2
- * experts are predicted from the pre-attention residual before the router
- * runs, and the predicted experts' weights are loaded early).  Here every
- * workgroup scores the router on the layer's pre-attention residual after its
- * QKV rows, and the instruction before its gate/up tile stages the predicted
- * expert's first rows of that tile in LDS.  The real router always decides:
+/* Speculative expert prediction for MoE models (epic-kernel README,
+ * "Speculative expert prediction": the top-2 experts are predicted from the
+ * pre-attention residual before the router runs, and the predicted experts'
+ * weights are loaded early), on (1) or off (0, the default) for launches
+ * enqueued after this call.  When on, every workgroup scores the router on
+ * the layer's pre-attention residual right after its QKV rows are stored,
+ * and the instruction before its gate/up tile stages the predicted expert's
+ * first rows of that tile in LDS (as many 1 KiB units per wavefront as the
+ * LDS plan, and mkd_set_lds_limits, allow).  The real router always decides:
  * a tile whose routed expert was predicted starts from the staged rows, any
  * other streams all of its rows, so the result never depends on the
- * prediction.  *predictions: gate/up tiles that had a prediction; *hits:
- * those whose routed expert it named.  Both 0 for dense models or when
- * staging is off (mkd_set_lds_limits with max_staged_units 0). */
+ * prediction.  It is off by default because on this part the staging loads
+ * slow the attention phase by about as much as they save in the expert
+ * stream.  No effect on dense models.  MKD_E_INVALID for a null model or
+ * `on` other than 0 or 1. */
+int mkd_set_expert_prediction(mkd_model* m, int32_t on);
+
+/* Outcome of the expert prediction (mkd_set_expert_prediction) over the last
+ * launch mkd_wait saw end.  *predictions: gate/up tiles that had a
+ * prediction; *hits: those whose routed expert it named.  Both 0 for dense
+ * models, with the prediction off, or when no weight units are staged
+ * (mkd_set_lds_limits with max_staged_units 0). */
 int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions);
 
 /* Limits on the per-workgroup LDS plan of schedules built or loaded after

@@ -38,7 +38,8 @@ EXPORTS = ("mkd_version", "mkd_last_error", "mkd_config_check", "mkd_weight_coun
            "mkd_workspace_bytes", "mkd_workspace_layout", "mkd_init", "mkd_init_batch", "mkd_init_static",
            "mkd_device_info", "mkd_lds_plan", "mkd_build_schedule", "mkd_load_schedule", "mkd_decode",
            "mkd_decode_batch", "mkd_wait", "mkd_abort", "mkd_set_watchdog",
-           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_read_probe", "mkd_spec_stats", "mkd_set_lds_limits",
+           "mkd_set_trace", "mkd_kernel_ms", "mkd_clock_hz", "mkd_read_probe", "mkd_set_expert_prediction", "mkd_spec_stats",
+           "mkd_set_lds_limits",
            "mkd_set_launch_mode", "mkd_destroy")
 
 # regions of a workspace, in mkd_workspace_layout's order
@@ -113,6 +114,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "mkd_set_trace": ([P, P, SZ], ctypes.c_int),
         "mkd_kernel_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mkd_clock_hz": ([P, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "mkd_set_expert_prediction": ([P, I32], ctypes.c_int),
         "mkd_spec_stats": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], ctypes.c_int),
         "mkd_read_probe": ([P, SZ, P, P], ctypes.c_int),
         "mkd_set_lds_limits": ([P, I32, I32], ctypes.c_int),
@@ -341,6 +343,10 @@ def mkd_read_probe(buf, sink, stream=None) -> None:
         stream = torch.cuda.current_stream().cuda_stream
     nbytes = buf.numel() * buf.element_size()
     _check(load().mkd_read_probe(_ptr(buf), nbytes, _ptr(sink), stream))
+
+
+def mkd_set_expert_prediction(m: int, on: bool) -> None:
+    _check(load().mkd_set_expert_prediction(m, 1 if on else 0))
 
 
 def mkd_spec_stats(m: int):

@@ -78,6 +78,7 @@ struct mkd_model {
   int32_t s_qkv = 0, s_part = 0;  // per-sequence strides of qkv and part (words)
   int flag_stride = 0;
   int x_cap = 0, pre_cap = -1;     // mkd_set_lds_limits
+  bool predict = false;            // mkd_set_expert_prediction (MoE models)
   bool plain_launch = false;       // mkd_set_launch_mode
   bool static_ws = false;          // the workspace is the library's static array (mkd_init_static)
   int32_t spec_hit = 0, spec_n = 0;  // expert predictions of the last waited-for launch
@@ -832,7 +833,8 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   p.x_floats = m->x_floats;
   p.out_floats = m->out_floats;
   p.res_floats = m->res_floats;
-  p.pre_units = m->pre_units;
+  // MoE models stage weight units only for the expert prediction, when it is on
+  p.pre_units = c->n_experts > 0 && !m->predict ? 0 : m->pre_units;
   p.pre_off = m->pre_off;
   p.eps = c->rms_eps;
   const char* why = "";
@@ -920,6 +922,13 @@ int mkd_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* 
   const char* why = "";
   const int rc = read_probe(buf_dev, bytes, sink_dev, stream, &why);
   return rc == MKD_OK ? MKD_OK : fail(rc, why);
+}
+
+int mkd_set_expert_prediction(mkd_model* m, int32_t on) {
+  if (!m) return fail(MKD_E_INVALID, "null model");
+  if (on != 0 && on != 1) return fail(MKD_E_INVALID, "on must be 0 or 1");
+  m->predict = on != 0;
+  return MKD_OK;
 }
 
 int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions) {

@@ -1118,6 +1118,125 @@ struct RowCursor {
   }
 };
 
+// ---------------------------------------------------------------- expert prediction, fast form
+
+// Speculative expert prediction (epic-kernel README, "Speculative expert
+// prediction": the top-2 experts are predicted from the pre-attention
+// residual before the router runs, and the predicted experts' weights are
+// loaded early).  sflag words of the prediction and of the staged expert.
+constexpr int kPredA = 5, kPredB = 6, kStagedExpert = 7;
+
+// Whether a MoE layer's prediction can run from LDS: its router rows (one
+// per wavefront) and FFN-norm gains fit past the QKV input, in whole 1 KiB
+// units, and the QKV row length takes the compile-time streamer.
+__device__ __forceinline__ bool predict_in_lds(CKParams& p) {
+  const int nseg = (p.d + 511) >> 9;
+  return p.pre_units > 0 && p.E <= kWaves && (p.d & 7) == 0 && p.d <= kThreads * 8 &&
+         (nseg == 1 || nseg == 2 || nseg == 4 || nseg == 6 || nseg == 8) &&
+         p.pre_off + (p.E + 1) * nseg * 256 + kWaves * kWaves <= p.x_floats;
+}
+
+// Request layer l's router rows (wavefront w < E: row w) and FFN-norm gains
+// (wavefront s < nseg: unit s) into LDS past the QKV input, each row padded
+// with zeros to whole 512-element units: 16-byte loads that write LDS
+// directly.  They complete with the loads issued after them (in order), so
+// the QKV streamer's wait for its inputs covers them.
+__device__ __forceinline__ void preload_router(Ctx& c, int l) {
+  CKParams& p = c.p;
+  const int nseg = (p.d + 511) >> 9;
+  const uint32_t rbytes = (uint32_t)p.d * 2u;
+  __attribute__((address_space(3))) char* base = (__attribute__((address_space(3))) char*)(c.xs + p.pre_off);
+  if (c.wave < p.E) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(lptr(p, l, WL_ROUTER) + (size_t)c.wave * p.d, rbytes);
+    for (int s = 0; s < nseg; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base + (c.wave * nseg + s) * 1024, 16, c.lane * 16, s * 1024, 0, 0);
+  }
+  if (c.wave < nseg) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(lptr(p, l, WL_FFN_NORM), rbytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base + (p.E * nseg + c.wave) * 1024, 16, c.lane * 16,
+                                             c.wave * 1024, 0, 0);
+  }
+}
+
+// The prediction itself, after the QKV outputs are stored: xs still holds
+// the layer's input residual h.  Expert e scores sum_i W_r[e,i] g_i h_i
+// (g: FFN-norm gains); RMSNorm's positive scale is left out, as it cannot
+// change the ranking.  Thread t takes elements 8t .. 8t + 7 of every expert
+// row; the top two (larger first, lower index on ties, the router's rule)
+// go to sflag.  Every wavefront's preload landed before the barrier ahead
+// of the QKV epilogue (each had waited for all its loads).
+__device__ __forceinline__ void predict_from_lds(Ctx& c) {
+  CKParams& p = c.p;
+  const int nseg = (p.d + 511) >> 9;
+  const int npad = nseg * 512;
+  const uint16_t* rows = (const uint16_t*)(c.xs + p.pre_off);
+  const uint16_t* gam = rows + (size_t)p.E * npad;
+  float* part = c.xs + p.pre_off + (p.E + 1) * nseg * 256;   // [wave][expert]
+  const int i0 = c.tid * 8;
+  float z[kWaves];
+#pragma unroll
+  for (int e = 0; e < kWaves; ++e) z[e] = 0.f;
+  if (i0 < p.d) {
+    const f32x4 h0 = *(const f32x4*)(c.xs + i0);
+    const f32x4 h1 = *(const f32x4*)(c.xs + i0 + 4);
+    const u32x4 gw = *(const u32x4*)(gam + i0);
+    const float hg[8] = {h0.x * bf_lo(gw.x), h0.y * bf_hi(gw.x), h0.z * bf_lo(gw.y), h0.w * bf_hi(gw.y),
+                         h1.x * bf_lo(gw.z), h1.y * bf_hi(gw.z), h1.z * bf_lo(gw.w), h1.w * bf_hi(gw.w)};
+#pragma unroll
+    for (int e = 0; e < kWaves; ++e) {
+      if (e < p.E) {
+        const u32x4 w = *(const u32x4*)(rows + (size_t)e * npad + i0);
+        float acc = bf_lo(w.x) * hg[0];
+        acc = fmaf(bf_hi(w.x), hg[1], acc);
+        acc = fmaf(bf_lo(w.y), hg[2], acc);
+        acc = fmaf(bf_hi(w.y), hg[3], acc);
+        acc = fmaf(bf_lo(w.z), hg[4], acc);
+        acc = fmaf(bf_hi(w.z), hg[5], acc);
+        acc = fmaf(bf_lo(w.w), hg[6], acc);
+        acc = fmaf(bf_hi(w.w), hg[7], acc);
+        z[e] = acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kWaves; ++e) {
+    if (e < p.E) {
+      const float sum = wave_sum(z[e]);
+      if (c.lane == 0) part[c.wave * kWaves + e] = sum;
+    }
+  }
+  __syncthreads();
+  if (c.tid == 0) {
+    // (unrolled over kWaves so that the scores stay in registers)
+    float zs[kWaves];
+#pragma unroll
+    for (int e = 0; e < kWaves; ++e) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += part[w * kWaves + e];
+      zs[e] = v;
+    }
+    int ea = 0;
+    float va = zs[0];
+#pragma unroll
+    for (int e = 1; e < kWaves; ++e)
+      if (e < p.E && zs[e] > va) {
+        ea = e;
+        va = zs[e];
+      }
+    int eb = -1;
+    float vb = 0.f;
+#pragma unroll
+    for (int e = 0; e < kWaves; ++e)
+      if (e < p.E && e != ea && (eb < 0 || zs[e] > vb)) {
+        eb = e;
+        vb = zs[e];
+      }
+    c.sflag[kPredA] = ea;
+    c.sflag[kPredB] = eb;
+  }
+}
+
 // Row length NSEG x 512 (rows shorter by less than 512 read zeros past
 // their end).  Each lane keeps its 8-element slices of the input vector for
 // all NSEG segments in registers, so a 1 KiB weight unit costs 16 VALU
@@ -1131,7 +1250,8 @@ struct RowCursor {
 // the end use a zero-size descriptor), which keeps the compiler's waits
 // exact: each row waits only for its own loads.
 template <int NSEG>
-__device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b, int index) {
+__device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b, int index,
+                                             bool predict = false) {
   constexpr int RROWS = 16 / NSEG > 1 ? 16 / NSEG : 1;
   constexpr int HROWS = RROWS / 2 > 1 ? RROWS / 2 : 1;
   CKParams& p = c.p;
@@ -1141,6 +1261,11 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   const uint16_t* gamma;
   bool embed_x, embed_res;
   gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
+  // MoE QKV: the router rows and FFN gains of the layer's expert prediction
+  // go to LDS first, so they arrive with the inputs (issued ahead of every
+  // other load here: LDS accesses that the compiler orders after them then
+  // wait for nothing younger)
+  if (predict) preload_router(c, l);
   const int lane = c.lane;
   const uint32_t rbytes = (uint32_t)g.K * 2u;
   const int ns = g.R * wave_rows(b - a, c.wave);   // stream rows of this wavefront
@@ -1253,6 +1378,8 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   }
   __syncthreads();
   gemv_epilogue<1>(c, op, l, a, b, index, tag);
+  // (the outputs are on their way; the prediction is off the path to them)
+  if (predict) predict_from_lds(c);
   return true;
 }
 
@@ -1640,7 +1767,8 @@ __device__ __forceinline__ void stage_upgate_b(Ctx& c, int l, int a, int b) {
 // dense GEMV opcodes: several sequences (batched kernel) by their count;
 // one sequence by the compile-time row length when there is one
 template <bool BATCHED>
-__device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b, int index) {
+__device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b, int index,
+                                            bool predict = false) {
   CKParams& p = c.p;
   if constexpr (BATCHED) {
     switch (c.B) {
@@ -1655,23 +1783,19 @@ __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b,
   }
   const int K = op == OP_OPROJ ? p.qd : (op == OP_DOWN ? p.F : p.d);
   switch ((K + 511) >> 9) {
-    case 1: return op_gemv_fast<1>(c, op, l, a, b, index);
-    case 2: return op_gemv_fast<2>(c, op, l, a, b, index);
-    case 4: return op_gemv_fast<4>(c, op, l, a, b, index);
-    case 6: return op_gemv_fast<6>(c, op, l, a, b, index);
-    case 8: return op_gemv_fast<8>(c, op, l, a, b, index);
+    case 1: return op_gemv_fast<1>(c, op, l, a, b, index, predict);
+    case 2: return op_gemv_fast<2>(c, op, l, a, b, index, predict);
+    case 4: return op_gemv_fast<4>(c, op, l, a, b, index, predict);
+    case 6: return op_gemv_fast<6>(c, op, l, a, b, index, predict);
+    case 8: return op_gemv_fast<8>(c, op, l, a, b, index, predict);
     default: return op_gemv(c, op, l, a, b, index);
   }
 }
 
 // ---------------------------------------------------------------- opcodes: MoE
 
-// Speculative expert prediction (epic-kernel README, "Speculative expert
-// prediction": the top-2 experts are predicted from the pre-attention
-// residual before the router runs, and the predicted experts' weights are
-// loaded early).  LDS words of the prediction and of its outcome counts.
-constexpr int kPredA = 5, kPredB = 6, kStagedExpert = 7;   // sflag words
-constexpr int kSpecHitWord = 252, kSpecNWord = 253;         // int words of the reduction scratch
+// counts of the expert prediction's outcomes, in int words of the reduction scratch
+constexpr int kSpecHitWord = 252, kSpecNWord = 253;
 // The route of a layer (experts a and b as int bits, their weights) in words
 // kRouteWords .. + 3 of the reduction scratch, and at kRouteStamp the tag of
 // the step and layer it belongs to (0: none yet)
@@ -1693,12 +1817,13 @@ __device__ __forceinline__ void desc_moe_upgate(CKParams& p, int l, int a, int w
   g.s1 = p.F; g.s2 = kNoSplit; g.K = p.d; g.R = 2; g.xoff1 = 0; g.a = a; g.w = w;
 }
 
-// After the layer's QKV rows, while xs still holds the layer's input
-// residual h (the QKV streamers keep their normalised copy in registers):
+// The general form of the prediction (where predict_in_lds does not hold):
+// after the layer's QKV rows, while xs still holds the layer's input
+// residual h (the QKV streamers keep their normalised copy in registers),
 // score the router on rmsnorm(h) with the FFN norm's gains -- one expert row
-// per wavefront -- and keep the top two (same order and tie rule as the
-// router) in LDS.  xs is free to overwrite: the next instructions fetch their
-// own inputs.
+// per wavefront, read from memory now -- and keep the top two (same order and
+// tie rule as the router) in LDS.  xs is free to overwrite: the next
+// instructions fetch their own inputs.
 __device__ __forceinline__ void predict_experts(Ctx& c, int l) {
   CKParams& p = c.p;
   const uint16_t* gamma = lptr(p, l, WL_FFN_NORM);
@@ -2390,6 +2515,7 @@ __device__ __forceinline__ void megakernel_body() {
       const int32_t* nx = i + 1 < n ? ins + kWords : nullptr;
       const int nxop = nx ? ldc_i32(nx + I_OP) : OP_NOP;
       const bool stage = p.pre_units > 0 && nxop == (MOE ? OP_MOE_UPGATE : OP_UPGATE);
+      const bool pfast = MOE && op == OP_QKV && predict_in_lds(p);
       if (stage && op == OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
         else if constexpr (MOE) stage_predicted(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
@@ -2400,7 +2526,7 @@ __device__ __forceinline__ void megakernel_body() {
         case OP_OPROJ:
         case OP_UPGATE:
         case OP_DOWN:
-        case OP_LMHEAD: ok = op_gemv_any<BATCHED>(c, op, l, a, b, index); break;
+        case OP_LMHEAD: ok = op_gemv_any<BATCHED>(c, op, l, a, b, index, pfast); break;
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
         case OP_MOE_UPGATE:
@@ -2413,8 +2539,9 @@ __device__ __forceinline__ void megakernel_body() {
       }
       if (ok) signal_done(c);
       if constexpr (MOE) {
-        // the expert prediction of this layer, while xs still holds its input residual
-        if (ok && op == OP_QKV && p.pre_units > 0) predict_experts(c, l);
+        // the expert prediction of this layer, while xs still holds its input
+        // residual (the fast form ran inside the QKV instruction)
+        if (ok && op == OP_QKV && p.pre_units > 0 && !pfast) predict_experts(c, l);
       }
       if (ok && stage && op != OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));

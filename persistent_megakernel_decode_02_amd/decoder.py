@@ -19,11 +19,12 @@ class Decoder:
     the other, and decoding goes through ``decode_batch``.  ``cooperative``
     False dispatches the same grid without the cooperative flag (profiling);
     ``lds_limits`` = (max input floats, max staged units) is passed to
-    mkd_set_lds_limits before the schedule is built (tests)."""
+    mkd_set_lds_limits before the schedule is built (tests);
+    ``expert_prediction`` turns on mkd_set_expert_prediction (MoE models)."""
 
     def __init__(self, cfg, weights: Sequence[torch.Tensor], kv_cache: torch.Tensor, max_seq: int,
                  n_wg: int = 0, n_chunks: int = 0, device: Optional[int] = None, batch: int = 1,
-                 cooperative: bool = True, lds_limits=None):
+                 cooperative: bool = True, lds_limits=None, expert_prediction: bool = False):
         self.cfg = cfg
         self.ccfg = capi.make_config(cfg)
         self.weights = list(weights)
@@ -52,6 +53,8 @@ class Decoder:
             capi.mkd_set_launch_mode(self.handle, False)
         if lds_limits is not None:
             capi.mkd_set_lds_limits(self.handle, *lds_limits)
+        if expert_prediction:
+            capi.mkd_set_expert_prediction(self.handle, True)
         self.schedule = capi.mkd_build_schedule(self.handle, n_wg, n_chunks, want_words=True)
 
     @property

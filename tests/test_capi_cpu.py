@@ -302,3 +302,11 @@ def test_read_probe_rejects_bad_arguments_before_any_device_call():
     assert lib.mkd_read_probe(ctypes.c_void_p(4096), 15, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID
     assert lib.mkd_read_probe(ctypes.c_void_p(4096), 0, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID
     assert lib.mkd_read_probe(ctypes.c_void_p(4104), 64, ctypes.c_void_p(4096), None) == capi.MKD_E_INVALID
+
+
+def test_control_calls_reject_a_null_model():
+    """The per-model switches check their handle on the host."""
+    lib = capi.load()
+    assert lib.mkd_set_expert_prediction(None, 1) == capi.MKD_E_INVALID
+    assert lib.mkd_set_lds_limits(None, 0, -1) == capi.MKD_E_INVALID
+    assert lib.mkd_set_launch_mode(None, 1) == capi.MKD_E_INVALID

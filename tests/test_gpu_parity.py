@@ -188,20 +188,20 @@ def test_moe_expert_prediction_never_changes_the_result(name, n_wg):
     """MoE models predict each layer's experts from the pre-attention residual
     and stage the predicted expert's first gate/up rows early; the routed
     expert is always the router's.  Launches with the prediction on and off
-    (staged units limited to 0) must be bit-identical, and the prediction
-    counts must cover every gate/up tile that lies in one expert's half."""
+    (the default) must be bit-identical, and the prediction counts must
+    cover every gate/up tile that lies in one expert's half."""
     cfg = synth.PRESETS.get(name) or EXTRA_SHAPES[name]
     T0, N = 40, 12
     w_gpu, kv_gpu = _setup(cfg, T0 + N, T0, gain_std=0.1)
     kv0 = kv_gpu.clone()
     first = synth.gen_tokens(1, cfg.vocab, stream=8)[0]
-    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1)
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1, expert_prediction=True)
     t_on, l_on = dec.decode(first, T0, N)
     hits, preds = capi.mkd_spec_stats(dec.handle)
     dec.close()
     kv_on = kv_gpu.clone()
     kv_gpu.copy_(kv0)
-    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1, lds_limits=(0, 0))
+    dec = Decoder(cfg, w_gpu, kv_gpu, T0 + N, n_wg=n_wg, n_chunks=1)   # off: the default
     t_off, l_off = dec.decode(first, T0, N)
     assert capi.mkd_spec_stats(dec.handle) == (0, 0)
     dec.close()

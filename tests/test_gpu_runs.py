@@ -24,6 +24,7 @@ import torch
 
 import synth
 from oracle import model as om
+from persistent_megakernel_decode_02_amd import capi
 from persistent_megakernel_decode_02_amd.decoder import Decoder
 from persistent_megakernel_decode_02_amd.tuning import launch_config
 from tests.gpu_common import check_run, close_enough, require_gpu, say
@@ -140,6 +141,14 @@ def test_mixtral_kv1024():
     toks, logits = dec.decode(first, T0, N)
     toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
     kv_new = kv_gpu[:, :, :, T0:T0 + N].float().cpu().numpy()
+    # the same launch with the expert prediction on (it rewrites the same
+    # cache positions with the same values): bit-identical results
+    capi.mkd_set_expert_prediction(dec.handle, True)
+    toks_p, logits_p = dec.decode(first, T0, N)
+    hits, preds = capi.mkd_spec_stats(dec.handle)
+    say(f"mixtral: with the expert prediction, {hits} of {preds} gate/up tiles had their expert predicted")
+    assert preds > 0
+    assert np.array_equal(toks_p.cpu().numpy(), toks) and np.array_equal(logits_p.cpu().numpy(), logits)
     dec.close()
     del kv_gpu
     probe = synth.gen_weights(cfg, device="cpu", only=[4])[4]
