@@ -249,8 +249,8 @@ int mkd_device_info(mkd_model* m, int32_t* n_cu, int32_t* max_coop_wg);
  * (0 = an area of their own after the others), total bytes}.  The staged
  * units are the next instruction's weights loaded ahead of it (epic-kernel
  * README, "L2 prefetching overlapped with prior instructions"), while the
- * workgroup waits out the attention phase: dense gate/up rows, or for MoE
- * models the predicted expert's gate/up rows (mkd_spec_stats).
+ * workgroup waits out the attention phase: dense gate/up rows (MoE models
+ * stage none).
  * MKD_E_INVALID for a bad config or argument. */
 int mkd_lds_plan(const mkd_config* cfg, int32_t batch, int32_t n_wg, int32_t n_chunks, int32_t lds_max,
                  int32_t* out);
@@ -368,24 +368,24 @@ int mkd_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* 
  * "Speculative expert prediction": the top-2 experts are predicted from the
  * pre-attention residual before the router runs, and the predicted experts'
  * weights are loaded early), on (1) or off (0, the default) for launches
- * enqueued after this call.  When on, every workgroup scores the router on
- * the layer's pre-attention residual right after its QKV rows are stored,
- * and the instruction before its gate/up tile stages the predicted expert's
- * first rows of that tile in LDS (as many 1 KiB units per wavefront as the
- * LDS plan, and mkd_set_lds_limits, allow).  The real router always decides:
- * a tile whose routed expert was predicted starts from the staged rows, any
- * other streams all of its rows, so the result never depends on the
- * prediction.  It is off by default because on this part the staging loads
- * slow the attention phase by about as much as they save in the expert
- * stream.  No effect on dense models.  MKD_E_INVALID for a null model or
+ * enqueued after this call.  When on, the workgroup holding a layer's
+ * O-projection tile 0 first scores the router on the layer's pre-attention
+ * residual and publishes the top two; every O-projection tile followed by a
+ * gate/up tile on its workgroup fetches them, and that gate/up tile requests
+ * the predicted expert's rows before it waits for its inputs.  The real
+ * router always decides: a tile whose routed expert was predicted keeps the
+ * requested rows, any other starts again on the routed expert's, so the
+ * result never depends on the prediction.  It is off by default because on
+ * this part it costs slightly more than it saves (about 0.2-0.5% on the
+ * Mixtral shape).  No effect on dense models, or on MoE models with more
+ * than 8 experts or d_model above 4096.  MKD_E_INVALID for a null model or
  * `on` other than 0 or 1. */
 int mkd_set_expert_prediction(mkd_model* m, int32_t on);
 
 /* Outcome of the expert prediction (mkd_set_expert_prediction) over the last
  * launch mkd_wait saw end.  *predictions: gate/up tiles that had a
  * prediction; *hits: those whose routed expert it named.  Both 0 for dense
- * models, with the prediction off, or when no weight units are staged
- * (mkd_set_lds_limits with max_staged_units 0). */
+ * models and with the prediction off. */
 int mkd_spec_stats(mkd_model* m, int32_t* hits, int32_t* predictions);
 
 /* Limits on the per-workgroup LDS plan of schedules built or loaded after

@@ -560,16 +560,7 @@ constexpr size_t kLdsSlack = 256;  // static LDS of the kernel and a margin
 // that the passes can be exercised on small models.
 static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int batch, int lds_max,
                   const LdsCaps& caps) {
-  if (batch == 1) {
-    // MoE: the input area grows to the LDS left over; its part past the
-    // O-projection's and gate/up's inputs holds the predicted expert's rows
-    if (c->n_experts == 0 || lds_max <= 0) return;
-    const size_t other = lds_bytes(p) - (size_t)p.x_floats * sizeof(float);
-    if (other + kLdsSlack >= (size_t)lds_max) return;
-    const int fill = (int)(((size_t)lds_max - kLdsSlack - other) / sizeof(float)) & ~3;
-    if (fill > p.x_floats) p.x_floats = fill;
-    return;
-  }
+  if (batch == 1) return;
   if (caps.x_cap > 0) {
     const int seg = 64 * (8 * batch + 4);   // one 512-element segment of every sequence, padded
     const int cap = caps.x_cap / seg * seg;
@@ -600,21 +591,10 @@ static void fit_x(KParams& p, const mkd_config* c, int n_chunks, int n_lm, int b
 // projection's longer input reuses that space after gate/up has read them.
 static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max, const LdsCaps& caps) {
   p.pre_off = 0;
-  if (batch == 1 && c->n_experts > 0) {
-    // MoE: the predicted expert's first gate/up rows, in the input area past
-    // the O-projection's and gate/up's inputs (the down projection's two-expert
-    // input reuses it afterwards); only where the router scoring of the
-    // prediction has its fast form (one expert row per wavefront, d <= 4096)
+  if (c->n_experts > 0) {
+    // MoE: nothing is staged (the expert prediction requests its rows into
+    // registers at the start of the gate/up tile)
     p.pre_units = 0;
-    if (c->n_experts > kWaves || c->d_model > 4096) return;
-    const int qd = c->n_q_heads * c->head_dim;
-    const int off = (std::max(vec_floats(c->d_model, 1), vec_floats(qd, 1)) + 3) & ~3;
-    if (off >= p.x_floats) return;
-    int n = std::min((p.x_floats - off) / (kWaves * 256), kPreMax);
-    if (caps.pre_cap >= 0 && caps.pre_cap < n) n = caps.pre_cap;
-    if (n < 1) return;
-    p.pre_off = off;
-    p.pre_units = n;
     return;
   }
   if (batch == 1) {
@@ -622,7 +602,6 @@ static void set_pre(KParams& p, const mkd_config* c, int batch, int lds_max, con
     return;
   }
   p.pre_units = 0;
-  if (c->n_experts > 0) return;
   // measured: with the down projection in passes over K (larger batches)
   // staging slows the step down
   if (p.x_floats < vec_floats(c->d_ff, batch)) return;
@@ -833,9 +812,10 @@ static int decode_launch(mkd_model* m, const int32_t* first_tokens, const int32_
   p.x_floats = m->x_floats;
   p.out_floats = m->out_floats;
   p.res_floats = m->res_floats;
-  // MoE models stage weight units only for the expert prediction, when it is on
-  p.pre_units = c->n_experts > 0 && !m->predict ? 0 : m->pre_units;
+  p.pre_units = m->pre_units;
   p.pre_off = m->pre_off;
+  // the prediction's router scoring takes one expert row per wavefront, d <= 4096
+  p.predict = m->predict && c->n_experts > 0 && c->n_experts <= kWaves && c->d_model <= 4096;
   p.eps = c->rms_eps;
   const char* why = "";
   const int rc = launch(p, m->ll_words, stream, m->k0, m->k1, !m->plain_launch, &why);

@@ -718,6 +718,14 @@ struct RowStream {
     }
     return v;
   }
+  // back to the first streamed unit, with the rows the map gives now (the
+  // map's matrices were changed); the ring's old loads are not used
+  __device__ __forceinline__ void restart() {
+    ps = first;
+    pseg = first % nseg;
+    pk = first / nseg;
+    row = ps < S ? (const char*)m.row(pk) : nullptr;
+  }
   // the first min(S - first, RING) streamed units, issued before the
   // instruction's inputs are waited for
   __device__ __forceinline__ void prefetch() {
@@ -1118,122 +1126,31 @@ struct RowCursor {
   }
 };
 
-// ---------------------------------------------------------------- expert prediction, fast form
+// ---------------------------------------------------------------- expert prediction
 
 // Speculative expert prediction (epic-kernel README, "Speculative expert
 // prediction": the top-2 experts are predicted from the pre-attention
 // residual before the router runs, and the predicted experts' weights are
-// loaded early).  sflag words of the prediction and of the staged expert.
-constexpr int kPredA = 5, kPredB = 6, kStagedExpert = 7;
+// loaded early).  sflag words of the prediction a workgroup holds, and the
+// tag of the (step, layer) it belongs to.
+constexpr int kPredA = 5, kPredB = 6, kPredStamp = 7;
+// route words 4 and 5: the published prediction (experts a and b as int bits)
+constexpr int kPredWord = 4;
 
-// Whether a MoE layer's prediction can run from LDS: its router rows (one
-// per wavefront) and FFN-norm gains fit past the QKV input, in whole 1 KiB
-// units, and the QKV row length takes the compile-time streamer.
-__device__ __forceinline__ bool predict_in_lds(CKParams& p) {
-  const int nseg = (p.d + 511) >> 9;
-  return p.pre_units > 0 && p.E <= kWaves && (p.d & 7) == 0 && p.d <= kThreads * 8 &&
-         (nseg == 1 || nseg == 2 || nseg == 4 || nseg == 6 || nseg == 8) &&
-         p.pre_off + (p.E + 1) * nseg * 256 + kWaves * kWaves <= p.x_floats;
+// The O-projection fetches the layer's published prediction for the gate/up
+// tile that follows it: one 16-byte load of both words, requested once the
+// O-projection's inputs are in (the prediction was published during the
+// attention phase) and read after its outputs are stored.  A prediction
+// whose words are not current, or that names no valid pair, is dropped.
+__device__ __forceinline__ u32x4 pred_request(CKParams& p) {
+  return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.route + kPredWord, 16u), 0, 0, kSC1);
 }
-
-// Request layer l's router rows (wavefront w < E: row w) and FFN-norm gains
-// (wavefront s < nseg: unit s) into LDS past the QKV input, each row padded
-// with zeros to whole 512-element units: 16-byte loads that write LDS
-// directly.  They complete with the loads issued after them (in order), so
-// the QKV streamer's wait for its inputs covers them.
-__device__ __forceinline__ void preload_router(Ctx& c, int l) {
-  CKParams& p = c.p;
-  const int nseg = (p.d + 511) >> 9;
-  const uint32_t rbytes = (uint32_t)p.d * 2u;
-  __attribute__((address_space(3))) char* base = (__attribute__((address_space(3))) char*)(c.xs + p.pre_off);
-  if (c.wave < p.E) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(lptr(p, l, WL_ROUTER) + (size_t)c.wave * p.d, rbytes);
-    for (int s = 0; s < nseg; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base + (c.wave * nseg + s) * 1024, 16, c.lane * 16, s * 1024, 0, 0);
-  }
-  if (c.wave < nseg) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(lptr(p, l, WL_FFN_NORM), rbytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base + (p.E * nseg + c.wave) * 1024, 16, c.lane * 16,
-                                             c.wave * 1024, 0, 0);
-  }
-}
-
-// The prediction itself, after the QKV outputs are stored: xs still holds
-// the layer's input residual h.  Expert e scores sum_i W_r[e,i] g_i h_i
-// (g: FFN-norm gains); RMSNorm's positive scale is left out, as it cannot
-// change the ranking.  Thread t takes elements 8t .. 8t + 7 of every expert
-// row; the top two (larger first, lower index on ties, the router's rule)
-// go to sflag.  Every wavefront's preload landed before the barrier ahead
-// of the QKV epilogue (each had waited for all its loads).
-__device__ __forceinline__ void predict_from_lds(Ctx& c) {
-  CKParams& p = c.p;
-  const int nseg = (p.d + 511) >> 9;
-  const int npad = nseg * 512;
-  const uint16_t* rows = (const uint16_t*)(c.xs + p.pre_off);
-  const uint16_t* gam = rows + (size_t)p.E * npad;
-  float* part = c.xs + p.pre_off + (p.E + 1) * nseg * 256;   // [wave][expert]
-  const int i0 = c.tid * 8;
-  float z[kWaves];
-#pragma unroll
-  for (int e = 0; e < kWaves; ++e) z[e] = 0.f;
-  if (i0 < p.d) {
-    const f32x4 h0 = *(const f32x4*)(c.xs + i0);
-    const f32x4 h1 = *(const f32x4*)(c.xs + i0 + 4);
-    const u32x4 gw = *(const u32x4*)(gam + i0);
-    const float hg[8] = {h0.x * bf_lo(gw.x), h0.y * bf_hi(gw.x), h0.z * bf_lo(gw.y), h0.w * bf_hi(gw.y),
-                         h1.x * bf_lo(gw.z), h1.y * bf_hi(gw.z), h1.z * bf_lo(gw.w), h1.w * bf_hi(gw.w)};
-#pragma unroll
-    for (int e = 0; e < kWaves; ++e) {
-      if (e < p.E) {
-        const u32x4 w = *(const u32x4*)(rows + (size_t)e * npad + i0);
-        float acc = bf_lo(w.x) * hg[0];
-        acc = fmaf(bf_hi(w.x), hg[1], acc);
-        acc = fmaf(bf_lo(w.y), hg[2], acc);
-        acc = fmaf(bf_hi(w.y), hg[3], acc);
-        acc = fmaf(bf_lo(w.z), hg[4], acc);
-        acc = fmaf(bf_hi(w.z), hg[5], acc);
-        acc = fmaf(bf_lo(w.w), hg[6], acc);
-        acc = fmaf(bf_hi(w.w), hg[7], acc);
-        z[e] = acc;
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kWaves; ++e) {
-    if (e < p.E) {
-      const float sum = wave_sum(z[e]);
-      if (c.lane == 0) part[c.wave * kWaves + e] = sum;
-    }
-  }
-  __syncthreads();
-  if (c.tid == 0) {
-    // (unrolled over kWaves so that the scores stay in registers)
-    float zs[kWaves];
-#pragma unroll
-    for (int e = 0; e < kWaves; ++e) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += part[w * kWaves + e];
-      zs[e] = v;
-    }
-    int ea = 0;
-    float va = zs[0];
-#pragma unroll
-    for (int e = 1; e < kWaves; ++e)
-      if (e < p.E && zs[e] > va) {
-        ea = e;
-        va = zs[e];
-      }
-    int eb = -1;
-    float vb = 0.f;
-#pragma unroll
-    for (int e = 0; e < kWaves; ++e)
-      if (e < p.E && e != ea && (eb < 0 || zs[e] > vb)) {
-        eb = e;
-        vb = zs[e];
-      }
-    c.sflag[kPredA] = ea;
-    c.sflag[kPredB] = eb;
+__device__ __forceinline__ void pred_keep(Ctx& c, const u32x4& v, uint32_t tag) {
+  const int pa = (int)v.x, pb = (int)v.z;
+  if (v.y == tag && v.w == tag && pa >= 0 && pa < c.p.E && pb >= 0 && pb < c.p.E && pa != pb) {
+    c.sflag[kPredA] = pa;
+    c.sflag[kPredB] = pb;
+    c.sflag[kPredStamp] = (int)tag;
   }
 }
 
@@ -1251,7 +1168,7 @@ __device__ __forceinline__ void predict_from_lds(Ctx& c) {
 // exact: each row waits only for its own loads.
 template <int NSEG>
 __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b, int index,
-                                             bool predict = false) {
+                                             bool pred_fetch = false) {
   constexpr int RROWS = 16 / NSEG > 1 ? 16 / NSEG : 1;
   constexpr int HROWS = RROWS / 2 > 1 ? RROWS / 2 : 1;
   CKParams& p = c.p;
@@ -1261,11 +1178,6 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   const uint16_t* gamma;
   bool embed_x, embed_res;
   gemv_setup(c, op, l, a, b, tag, g, f, gamma, embed_x, embed_res);
-  // MoE QKV: the router rows and FFN gains of the layer's expert prediction
-  // go to LDS first, so they arrive with the inputs (issued ahead of every
-  // other load here: LDS accesses that the compiler orders after them then
-  // wait for nothing younger)
-  if (predict) preload_router(c, l);
   const int lane = c.lane;
   const uint32_t rbytes = (uint32_t)g.K * 2u;
   const int ns = g.R * wave_rows(b - a, c.wave);   // stream rows of this wavefront
@@ -1295,6 +1207,8 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   // everything requested so far has arrived (it was issued before the
   // inputs, and loads complete in order); saying so keeps the waits below exact
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  u32x4 pv = u32x4{0u, 0u, 0u, 0u};
+  if (pred_fetch && c.tid == 0) pv = pred_request(p);
   const bool deep = nq > HROWS;
   if (deep) {
 #pragma unroll
@@ -1378,8 +1292,7 @@ __device__ __forceinline__ bool op_gemv_fast(Ctx& c, int op, int l, int a, int b
   }
   __syncthreads();
   gemv_epilogue<1>(c, op, l, a, b, index, tag);
-  // (the outputs are on their way; the prediction is off the path to them)
-  if (predict) predict_from_lds(c);
+  if (pred_fetch && c.tid == 0) pred_keep(c, pv, tag);
   return true;
 }
 
@@ -1768,7 +1681,7 @@ __device__ __forceinline__ void stage_upgate_b(Ctx& c, int l, int a, int b) {
 // one sequence by the compile-time row length when there is one
 template <bool BATCHED>
 __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b, int index,
-                                            bool predict = false) {
+                                            bool pred_fetch = false) {
   CKParams& p = c.p;
   if constexpr (BATCHED) {
     switch (c.B) {
@@ -1783,11 +1696,11 @@ __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b,
   }
   const int K = op == OP_OPROJ ? p.qd : (op == OP_DOWN ? p.F : p.d);
   switch ((K + 511) >> 9) {
-    case 1: return op_gemv_fast<1>(c, op, l, a, b, index, predict);
-    case 2: return op_gemv_fast<2>(c, op, l, a, b, index, predict);
-    case 4: return op_gemv_fast<4>(c, op, l, a, b, index, predict);
-    case 6: return op_gemv_fast<6>(c, op, l, a, b, index, predict);
-    case 8: return op_gemv_fast<8>(c, op, l, a, b, index, predict);
+    case 1: return op_gemv_fast<1>(c, op, l, a, b, index, pred_fetch);
+    case 2: return op_gemv_fast<2>(c, op, l, a, b, index, pred_fetch);
+    case 4: return op_gemv_fast<4>(c, op, l, a, b, index, pred_fetch);
+    case 6: return op_gemv_fast<6>(c, op, l, a, b, index, pred_fetch);
+    case 8: return op_gemv_fast<8>(c, op, l, a, b, index, pred_fetch);
     default: return op_gemv(c, op, l, a, b, index);
   }
 }
@@ -1817,15 +1730,15 @@ __device__ __forceinline__ void desc_moe_upgate(CKParams& p, int l, int a, int w
   g.s1 = p.F; g.s2 = kNoSplit; g.K = p.d; g.R = 2; g.xoff1 = 0; g.a = a; g.w = w;
 }
 
-// The general form of the prediction (where predict_in_lds does not hold):
-// after the layer's QKV rows, while xs still holds the layer's input
-// residual h (the QKV streamers keep their normalised copy in registers),
-// score the router on rmsnorm(h) with the FFN norm's gains -- one expert row
-// per wavefront, read from memory now -- and keep the top two (same order and
-// tie rule as the router) in LDS.  xs is free to overwrite: the next
-// instructions fetch their own inputs.
-__device__ __forceinline__ void predict_experts(Ctx& c, int l) {
+// One workgroup per layer, the one holding O-projection tile 0 (it waits out
+// the attention phase anyway), predicts the layer's two experts and publishes
+// them for the gate/up tiles: the layer's input residual h (published before
+// the attention phase; for layer 0 the embedding row), RMSNorm with the FFN
+// norm's gains, router logits with one expert row per wavefront, and the top
+// two in the router's order and tie rule, in route words 4 and 5.
+__device__ __forceinline__ bool predict_publish(Ctx& c, int l) {
   CKParams& p = c.p;
+  const uint32_t tag = tag_of(p, c.t, l);
   const uint16_t* gamma = lptr(p, l, WL_FFN_NORM);
   const Gains gr = load_gains(c, p.d, gamma);
   constexpr int RU = 8;
@@ -1835,7 +1748,13 @@ __device__ __forceinline__ void predict_experts(Ctx& c, int l) {
   u32x4 rw[RU];
 #pragma unroll
   for (int k = 0; k < RU; ++k) rw[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (k * 64 + c.lane) * 16, 0, 0);
-  __syncthreads();                        // every wavefront is done with its QKV rows
+  if (l == 0) {
+    if (!embed_rows(c, 0, p.d, c.xs)) return false;
+    __syncthreads();
+  } else {
+    const Fetch f[1] = {{p.h, p.d, tag, c.xs}};
+    if (!gather<1>(c, f)) return false;
+  }
   rmsnorm_g(c, p.d, gamma, gr);
   if (p.d & 511) {
     pad_zero(c, c.xs, p.d);
@@ -1866,39 +1785,11 @@ __device__ __forceinline__ void predict_experts(Ctx& c, int l) {
     int eb = ea == 0 ? 1 : 0;
     for (int e = 0; e < p.E; ++e)
       if (e != ea && c.red[64 + e] > c.red[64 + eb]) eb = e;
-    c.sflag[kPredA] = ea;
-    c.sflag[kPredB] = eb;
+    ll_store(p.route + kPredWord, __int_as_float(ea), tag);
+    ll_store(p.route + kPredWord + 1, __int_as_float(eb), tag);
   }
   __syncthreads();
-}
-
-// Stage the first units of this wavefront's stream of the MoE gate/up tile
-// [a, b) of layer l for the predicted experts, in the input area past the
-// gate/up input (pre_area_b), and record which expert they belong to.  As
-// stage_upgate: issued while the workgroup waits out the attention phase, and
-// waited for on the spot.
-__device__ __forceinline__ void stage_predicted(Ctx& c, int l, int a, int b) {
-  CKParams& p = c.p;
-  const int pa = uni(c.sflag[kPredA]), pb = uni(c.sflag[kPredB]);
-  const int e = tile_expert(p, a, b, pa, pb);
-  if (c.tid == 0) c.sflag[kStagedExpert] = e;
-  if (e < 0) return;
-  GemvDesc g;
-  desc_moe_upgate(p, l, a, c.wave, pa, pb, g);
-  const GenMap m{g};
-  const int nseg = (g.K + 511) >> 9;
-  const int n = min(2 * wave_rows(b - a, c.wave) * nseg, p.pre_units);
-  __attribute__((address_space(3))) char* dst = (__attribute__((address_space(3))) char*)pre_area_b(c);
-  int k = 0, seg = 0;
-  for (int u = 0; u < n; ++u) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(m.row(k), (uint32_t)g.K * 2u);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + u * 1024, 16, c.lane * 16, seg * 1024, 0, kNT);
-    if (++seg == nseg) {
-      seg = 0;
-      ++k;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  return true;
 }
 
 __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int index) {
@@ -1923,6 +1814,20 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
 #pragma unroll
     for (int k = 0; k < RU; ++k) rw[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (k * 64 + c.lane) * 16, 0, 0);
   }
+  // With a prediction for this layer (fetched by the O-projection before
+  // it), the predicted expert's rows of this tile are requested before the
+  // inputs are waited for; the router then decides whether they are used.
+  int pa = -1, pb = -1;
+  if (p.predict && uni(c.sflag[kPredStamp]) == (int)tag) {
+    pa = uni(c.sflag[kPredA]);
+    pb = uni(c.sflag[kPredB]);
+  }
+  const int tp = pa >= 0 ? tile_expert(p, a, b, pa, pb) : -1;
+  GemvDesc g;
+  desc_moe_upgate(p, l, a, c.wave, tp >= 0 ? pa : 0, tp >= 0 ? pb : 1, g);
+  const GenMap m{g};
+  RowStream<GenMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane);
+  if (tp >= 0) rs.prefetch();
   const Fetch f[1] = {{p.hmid, p.d, tag, c.xs}};
   if (!gather_inputs<1>(c, f)) return false;
   rmsnorm_g(c, p.d, gamma, gr);
@@ -1982,26 +1887,21 @@ __device__ __forceinline__ bool op_moe_upgate(Ctx& c, int l, int a, int b, int i
   }
   __syncthreads();
   const int ea = uni(c.sflag[3]), eb = uni(c.sflag[4]);
-  // The rows the instruction before this one staged are used only when they
-  // are the routed expert's (the router decides; the prediction only moved
-  // some loads earlier).
-  int staged = 0;
-  if (p.pre_units > 0 && c.instr > 0) {
-    const int se = uni(c.sflag[kStagedExpert]);
-    const bool hit = se >= 0 && se == tile_expert(p, a, b, ea, eb);
-    if (hit) staged = min(2 * wave_rows(b - a, c.wave) * ((p.d + 511) >> 9), p.pre_units);
-    if (c.tid == 0 && se >= 0) {
-      int* cnt = (int*)c.red;
-      cnt[kSpecHitWord] += hit ? 1 : 0;
-      cnt[kSpecNWord] += 1;
-    }
+  // The requested rows are used only when they are the routed expert's (the
+  // router decides; the prediction only moved some loads earlier); else the
+  // stream starts again on the routed expert's rows.
+  const bool hit = tp >= 0 && tp == tile_expert(p, a, b, ea, eb);
+  if (tp >= 0 && c.tid == 0) {
+    int* cnt = (int*)c.red;
+    cnt[kSpecHitWord] += hit ? 1 : 0;
+    cnt[kSpecNWord] += 1;
   }
-  GemvDesc g;
-  desc_moe_upgate(p, l, a, c.wave, ea, eb, g);
-  const GenMap m{g};
-  RowStream<GenMap> rs(m, p.d, 2 * wave_rows(b - a, c.wave), c.lane, staged);
-  rs.prefetch();
-  rs.run(c.xs, c.out, pre_area_b(c));
+  if (!hit) {
+    desc_moe_upgate(p, l, a, c.wave, ea, eb, g);
+    rs.restart();
+    rs.prefetch();
+  }
+  rs.run(c.xs, c.out);
   __syncthreads();
   for (int i = c.tid; i < b - a; i += kThreads)
     ll_store(p.act + a + i, silu(c.out[2 * i]) * c.out[2 * i + 1], tag);
@@ -2468,7 +2368,7 @@ __device__ __forceinline__ void megakernel_body() {
     sflag[0] = 0;
     sflag[1] = 0;
     sflag[2] = -1;
-    sflag[kStagedExpert] = -1;
+    sflag[kPredStamp] = -1;
     ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecHitWord] = 0;
     ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kSpecNWord] = 0;
     if constexpr (MOE) ((int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats))[kRouteStamp] = 0;
@@ -2507,26 +2407,32 @@ __device__ __forceinline__ void megakernel_body() {
             sflag, wg, i, t, tid, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6),
             ldc_i32(ins + I_STAGE), index, tr, BATCHED ? ldc_i32(ins + I_SEQ) : 0, BATCHED ? p.B : 1};
       if (tr && tid == 0) st_u64(tr, wall_clock64());
-      // The first weight units of the next gate/up instruction (dense: its
-      // first rows; MoE: the predicted expert's) are staged in LDS by this
-      // one: at the start of an O-projection (whose wait spans the whole
-      // attention phase), else at the end of the instruction, once its own
-      // loads are done.
+      // The first weight units of the next dense gate/up instruction are
+      // staged in LDS by this one: at the start of an O-projection (whose
+      // wait spans the whole attention phase), else at the end of the
+      // instruction, once its own loads are done.
       const int32_t* nx = i + 1 < n ? ins + kWords : nullptr;
       const int nxop = nx ? ldc_i32(nx + I_OP) : OP_NOP;
-      const bool stage = p.pre_units > 0 && nxop == (MOE ? OP_MOE_UPGATE : OP_UPGATE);
-      const bool pfast = MOE && op == OP_QKV && predict_in_lds(p);
+      const bool stage = !MOE && p.pre_units > 0 && nxop == OP_UPGATE;
+      // MoE with the expert prediction on: O-projection tile 0 first predicts
+      // and publishes the layer's experts, and an O-projection followed by a
+      // gate/up tile fetches them
+      const bool predict = MOE && p.predict && op == OP_OPROJ;
       if (stage && op == OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
-        else if constexpr (MOE) stage_predicted(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
         else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
       }
-      switch (op) {
+      if constexpr (MOE) {
+        if (predict && index == 0) ok = predict_publish(c, l);
+      }
+      if (ok) switch (op) {
         case OP_QKV:
         case OP_OPROJ:
         case OP_UPGATE:
         case OP_DOWN:
-        case OP_LMHEAD: ok = op_gemv_any<BATCHED>(c, op, l, a, b, index, pfast); break;
+        case OP_LMHEAD:
+          ok = op_gemv_any<BATCHED>(c, op, l, a, b, index, predict && nxop == OP_MOE_UPGATE);
+          break;
         case OP_ATTN: ok = p.hd == 64 ? op_attn_hd<64>(c, l, a, b) : op_attn_hd<128>(c, l, a, b); break;
         case OP_AREDUCE: ok = op_areduce(c, l, a); break;
         case OP_MOE_UPGATE:
@@ -2538,21 +2444,15 @@ __device__ __forceinline__ void megakernel_body() {
         default: break;
       }
       if (ok) signal_done(c);
-      if constexpr (MOE) {
-        // the expert prediction of this layer, while xs still holds its input
-        // residual (the fast form ran inside the QKV instruction)
-        if (ok && op == OP_QKV && p.pre_units > 0 && !pfast) predict_experts(c, l);
-      }
       if (ok && stage && op != OP_OPROJ) {
         if constexpr (BATCHED) stage_upgate_b(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
-        else if constexpr (MOE) stage_predicted(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
         else stage_upgate(c, ldc_i32(nx + I_LAYER), ldc_i32(nx + I_A), ldc_i32(nx + I_B));
       }
     }
   }
   if constexpr (MOE) {
     // this workgroup's expert-prediction counts, summed over workgroups
-    if (pk->pre_units > 0 && threadIdx.x == 0) {
+    if (pk->predict && threadIdx.x == 0) {
       const int* cnt = (const int*)(smem + pk->x_floats + pk->res_floats + pk->out_floats);
       atomicAdd(pk->status + S_SPEC_HIT, cnt[kSpecHitWord]);
       atomicAdd(pk->status + S_SPEC_N, cnt[kSpecNWord]);

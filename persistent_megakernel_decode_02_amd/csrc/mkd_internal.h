@@ -110,11 +110,11 @@ struct KParams {
   int32_t out_floats;        // LDS floats for one instruction's GEMV row results
   int32_t res_floats;        // LDS floats for the residual rows of a tile (all sequences)
   int32_t pre_units;         // 1 KiB weight units per wavefront staged in LDS by the
-                             // instruction before their own (0 = none): dense gate/up rows,
-                             // or for MoE the predicted expert's first gate/up rows
+                             // instruction before their own (0 = none): dense gate/up rows
   int32_t pre_off;           // where those units sit: 0 = their own area after the reduction
                              // scratch; else this many floats into the input area, past the
-                             // gate/up and O-projection inputs (several sequences, MoE)
+                             // gate/up and O-projection inputs (several sequences)
+  int32_t predict;           // MoE: the speculative expert prediction is on
   float eps;
 };
 
