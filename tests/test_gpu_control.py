@@ -106,6 +106,24 @@ def test_watchdog_setting_is_validated():
     dec.close()
 
 
+def test_expert_prediction_setting_is_validated():
+    """mkd_set_expert_prediction takes 0 or 1; on a dense model it is accepted
+    and changes nothing (no predictions are counted)."""
+    require_gpu()
+    cfg, w, kv = _tiny(64, 32)
+    dec = Decoder(cfg, w, kv, 64)
+    ref, _ = dec.decode(3, 32, 4, want_logits=False)
+    for bad in (2, -1):
+        with pytest.raises(capi.MkdError) as e:   # (the binding passes only 0 or 1)
+            capi._check(capi.load().mkd_set_expert_prediction(dec.handle, bad))
+        assert e.value.code == capi.MKD_E_INVALID
+    capi.mkd_set_expert_prediction(dec.handle, True)
+    toks, _ = dec.decode(3, 32, 4, want_logits=False)
+    assert torch.equal(toks, ref)
+    assert capi.mkd_spec_stats(dec.handle) == (0, 0)
+    dec.close()
+
+
 def test_workspace_too_small_for_a_schedule_is_rejected():
     """A schedule whose instruction tensor and activations do not fit in the
     handle's workspace is refused on the host with the size it needs."""
