@@ -389,6 +389,42 @@ def trace_breakdown(dec, launch_and_wait, N, out_path=None, title=""):
         lines.append(f"| {op} | {a[0]:.1f} | {100 * a[0] / total:.1f} | {a[1]:.1f} | {a[2]:.1f} | {a[3]:.1f} | "
                      f"{a[4] / 1e6:.1f} | {gbs:.0f} | {100 * gbs / 8000:.1f} |")
     lines.append(f"| total | {total:.1f} | 100 | | | | | | |")
+    # when each stage's consumers start their instruction and hold their
+    # inputs, relative to the producing stage's last publish
+    rel = {}
+    chain = [0, 0]
+    members = {}
+    for w in range(n_wg):
+        for i in range(int(counts[w])):
+            members.setdefault(int(body[w, i, 2]), []).append((w, i))
+    for k in range(N):
+        for st in range(1, n_st):
+            m0, m1 = members[st - 1], members[st]
+            pubs0 = np.array([t[w, k, i, 2] for w, i in m0])
+            last = pubs0.max()
+            starts = np.array([t[w, k, i, 0] for w, i in m1])
+            rdys = np.array([t[w, k, i, 1] for w, i in m1])
+            r = rel.setdefault(opname[st], [[], []])
+            r[0].append((starts - last) * us)
+            r[1].append((rdys - last) * us)
+            if len(m1) > 8:
+                chain[1] += 1
+                chain[0] += m1[int(np.argmax(rdys))][0] == m0[int(np.argmax(pubs0))][0]
+    lines.append("")
+    lines.append("Consumers against the producing stage's last publish (us; negative: before it): when they start "
+                 "the instruction, and when they hold its inputs.")
+    lines.append("")
+    lines.append("| Opcode | start p10 | start median | start p90 | ready p10 | ready median | ready p90 | ready max |")
+    lines.append("|---|---|---|---|---|---|---|---|")
+    for op, (a, b) in sorted(rel.items()):
+        a, b = np.concatenate(a), np.concatenate(b)
+        pa, pb = np.percentile(a, [10, 50, 90]), np.percentile(b, [10, 50, 90])
+        lines.append(f"| {op} | {pa[0]:.2f} | {pa[1]:.2f} | {pa[2]:.2f} | {pb[0]:.2f} | {pb[1]:.2f} | {pb[2]:.2f} | "
+                     f"{b.max():.2f} |")
+    if chain[1]:
+        lines.append("")
+        lines.append(f"The last consumer to hold its inputs was the producing stage's last publisher in {chain[0]} of "
+                     f"{chain[1]} stage instances.")
     for ln in lines:
         log(ln)
     if out_path:
