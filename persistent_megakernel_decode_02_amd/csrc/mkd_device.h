@@ -1059,9 +1059,37 @@ __device__ __forceinline__ int staged_rows(Ctx& c, int op, int ns, int nseg) {
   return op == OP_UPGATE && c.instr > 0 ? min(ns, c.p.pre_units / nseg) : 0;
 }
 
+// ---------------------------------------------------------------- expert prediction
+
+// Speculative expert prediction (epic-kernel README, "Speculative expert
+// prediction": the top-2 experts are predicted from the pre-attention
+// residual before the router runs, and the predicted experts' weights are
+// loaded early).  sflag words of the prediction a workgroup holds, and the
+// tag of the (step, layer) it belongs to.
+constexpr int kPredA = 5, kPredB = 6, kPredStamp = 7;
+// route words 4 and 5: the published prediction (experts a and b as int bits)
+constexpr int kPredWord = 4;
+
+// The O-projection fetches the layer's published prediction for the gate/up
+// tile that follows it: one 16-byte load of both words, requested once the
+// O-projection's inputs are in (the prediction was published during the
+// attention phase) and read after its outputs are stored.  A prediction
+// whose words are not current, or that names no valid pair, is dropped.
+__device__ __forceinline__ u32x4 pred_request(CKParams& p) {
+  return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.route + kPredWord, 16u), 0, 0, kSC1);
+}
+__device__ __forceinline__ void pred_keep(Ctx& c, const u32x4& v, uint32_t tag) {
+  const int pa = (int)v.x, pb = (int)v.z;
+  if (v.y == tag && v.w == tag && pa >= 0 && pa < c.p.E && pb >= 0 && pb < c.p.E && pa != pb) {
+    c.sflag[kPredA] = pa;
+    c.sflag[kPredB] = pb;
+    c.sflag[kPredStamp] = (int)tag;
+  }
+}
+
 // Any row length: rows stream through the runtime-length RowStream, the
 // input vector is read from LDS per 1 KiB unit.
-__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index) {
+__device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int index, bool pred_fetch = false) {
   CKParams& p = c.p;
   const uint32_t tag = tag_of(p, c.t, op == OP_LMHEAD ? p.L : l);
   GemvDesc g;
@@ -1076,11 +1104,14 @@ __device__ __forceinline__ bool op_gemv(Ctx& c, int op, int l, int a, int b, int
   rs.prefetch();
   const Gains gr = load_gains(c, p.d, gamma ? gamma : wptr(p, W_FINAL_NORM));
   if (!gemv_inputs(c, a, b, g.K, f, embed_x, embed_res)) return false;
+  u32x4 pv = u32x4{0u, 0u, 0u, 0u};
+  if (pred_fetch && c.tid == 0) pv = pred_request(p);
   if (gamma) rmsnorm_g(c, p.d, gamma, gr);
   // staged units were written by this wavefront, which waited for them
   rs.run(c.xs, c.out, pre_area(c));
   __syncthreads();
   gemv_epilogue<1>(c, op, l, a, b, index, tag);
+  if (pred_fetch && c.tid == 0) pred_keep(c, pv, tag);
   return true;
 }
 
@@ -1125,34 +1156,6 @@ struct RowCursor {
     return q;
   }
 };
-
-// ---------------------------------------------------------------- expert prediction
-
-// Speculative expert prediction (epic-kernel README, "Speculative expert
-// prediction": the top-2 experts are predicted from the pre-attention
-// residual before the router runs, and the predicted experts' weights are
-// loaded early).  sflag words of the prediction a workgroup holds, and the
-// tag of the (step, layer) it belongs to.
-constexpr int kPredA = 5, kPredB = 6, kPredStamp = 7;
-// route words 4 and 5: the published prediction (experts a and b as int bits)
-constexpr int kPredWord = 4;
-
-// The O-projection fetches the layer's published prediction for the gate/up
-// tile that follows it: one 16-byte load of both words, requested once the
-// O-projection's inputs are in (the prediction was published during the
-// attention phase) and read after its outputs are stored.  A prediction
-// whose words are not current, or that names no valid pair, is dropped.
-__device__ __forceinline__ u32x4 pred_request(CKParams& p) {
-  return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(p.route + kPredWord, 16u), 0, 0, kSC1);
-}
-__device__ __forceinline__ void pred_keep(Ctx& c, const u32x4& v, uint32_t tag) {
-  const int pa = (int)v.x, pb = (int)v.z;
-  if (v.y == tag && v.w == tag && pa >= 0 && pa < c.p.E && pb >= 0 && pb < c.p.E && pa != pb) {
-    c.sflag[kPredA] = pa;
-    c.sflag[kPredB] = pb;
-    c.sflag[kPredStamp] = (int)tag;
-  }
-}
 
 // Row length NSEG x 512 (rows shorter by less than 512 read zeros past
 // their end).  Each lane keeps its 8-element slices of the input vector for
@@ -1701,7 +1704,7 @@ __device__ __forceinline__ bool op_gemv_any(Ctx& c, int op, int l, int a, int b,
     case 4: return op_gemv_fast<4>(c, op, l, a, b, index, pred_fetch);
     case 6: return op_gemv_fast<6>(c, op, l, a, b, index, pred_fetch);
     case 8: return op_gemv_fast<8>(c, op, l, a, b, index, pred_fetch);
-    default: return op_gemv(c, op, l, a, b, index);
+    default: return op_gemv(c, op, l, a, b, index, pred_fetch);
   }
 }
 

@@ -158,13 +158,17 @@ EXTRA_SHAPES = {
     # are fetched on their own, zero-padded to whole segments
     "tiny_moe_f768": synth.ModelConfig("tiny-moe-f768", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
                                        head_dim=64, d_ff=768, vocab=1024, n_experts=8, top_k=2, rope_theta=1e6),
+    # an attention width of three 512-element segments (12 q heads of 128, three
+    # per kv head): the O-projection takes the runtime-length streamer
+    "tiny_moe_q3": synth.ModelConfig("tiny-moe-q3", n_layers=2, d_model=256, n_q_heads=12, n_kv_heads=4,
+                                     head_dim=128, d_ff=512, vocab=1024, n_experts=8, top_k=2, rope_theta=1e6),
 }
 
 
 @pytest.mark.parametrize("name,n_wg,n_chunks", [("tiny_g1", 256, 1), ("tiny_g1", 40, 3), ("tiny_moe_e4", 256, 1),
                                                 ("tiny_moe_e4", 33, 2), ("tiny_moe_e16", 256, 1),
                                                 ("tiny_moe_e16", 64, 4), ("tiny_moe_f768", 256, 1),
-                                                ("tiny_moe_f768", 33, 2)])
+                                                ("tiny_moe_f768", 33, 2), ("tiny_moe_q3", 256, 1)])
 def test_accepted_shapes_beyond_the_presets(name, n_wg, n_chunks):
     cfg = EXTRA_SHAPES[name]
     T0, N = 50, 8
@@ -183,7 +187,7 @@ def test_accepted_shapes_beyond_the_presets(name, n_wg, n_chunks):
     assert ok, f"appended kv max err {mx}"
 
 
-@pytest.mark.parametrize("name,n_wg", [("tiny_moe", 256), ("tiny_moe", 33), ("tiny_moe_e4", 64)])
+@pytest.mark.parametrize("name,n_wg", [("tiny_moe", 256), ("tiny_moe", 33), ("tiny_moe_e4", 64), ("tiny_moe_q3", 64)])
 def test_moe_expert_prediction_never_changes_the_result(name, n_wg):
     """MoE models predict each layer's experts from the pre-attention residual
     and stage the predicted expert's first gate/up rows early; the routed
