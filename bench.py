@@ -321,19 +321,32 @@ def trace_breakdown(dec, launch_and_wait, N, out_path=None, title=""):
     publish to its own last publish, split into the transition (to its first
     consumer ready), the spread of its consumers becoming ready, and its work
     -- and the algorithmic bytes it moves in that time."""
-    import numpy as np
     import torch
     from persistent_megakernel_decode_02_amd import capi
     words = dec.schedule
-    cfg = dec.cfg
     n_wg, max_instr = int(words[2]), int(words[4])
     tr = torch.zeros(n_wg * N * max_instr * 4, dtype=torch.int64, device="cuda")
     capi.mkd_set_trace(dec.handle, tr)
     launch_and_wait()
     capi.mkd_set_trace(dec.handle, None)
     hz = capi.mkd_clock_hz(dec.handle)
+    lines = trace_tables(tr.cpu().numpy().reshape(n_wg, N, max_instr, 4), words, hz, dec.cfg, dec.trace_pos)
+    for ln in lines:
+        log(ln)
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(f"# Per-opcode cost: {title}\n\n" + "\n".join(lines) + "\n")
+
+
+def trace_tables(trace, words, hz, cfg, trace_pos):
+    """The tables of trace_breakdown from a launch's device trace: trace is
+    [workgroup][step][instruction][start, inputs ready, outputs published,
+    spare] in clock ticks of hz, words the launch's schedule words."""
+    import numpy as np
+    from persistent_megakernel_decode_02_amd import capi
+    n_wg, N, max_instr = trace.shape[0], trace.shape[1], int(words[4])
     us = 1e6 / hz
-    t = tr.cpu().numpy().reshape(n_wg, N, max_instr, 4).astype(np.float64)
+    t = np.asarray(trace).astype(np.float64)
     counts = words[16:16 + n_wg]
     body = words[16 + n_wg:].reshape(n_wg, max_instr, 16)
     n_st = int(words[3])
@@ -374,7 +387,7 @@ def trace_breakdown(dec, launch_and_wait, N, out_path=None, title=""):
             a[1] += max(0.0, rdy_min[k, st] - p0) * us          # transition
             a[2] += (rdy_max[k, st] - rdy_min[k, st]) * us      # consumer-ready spread
             a[3] += (pub[k, st] - rdy_max[k, st]) * us          # work after the last consumer was ready
-            a[4] += stage_bytes(cfg, op, dec.trace_pos + k)
+            a[4] += stage_bytes(cfg, op, trace_pos + k)
     total = sum(a[0] for a in acc.values()) / N
     lines.append("")
     lines.append(f"Per token (us, mean over {N} steps): each stage's share of the critical path (previous stage's "
@@ -425,11 +438,7 @@ def trace_breakdown(dec, launch_and_wait, N, out_path=None, title=""):
         lines.append("")
         lines.append(f"The last consumer to hold its inputs was the producing stage's last publisher in {chain[0]} of "
                      f"{chain[1]} stage instances.")
-    for ln in lines:
-        log(ln)
-    if out_path:
-        with open(out_path, "w") as f:
-            f.write(f"# Per-opcode cost: {title}\n\n" + "\n".join(lines) + "\n")
+    return lines
 
 
 if __name__ == "__main__":
