@@ -346,6 +346,7 @@ def mkd_read_probe(buf, sink, stream=None) -> None:
 
 
 def mkd_set_expert_prediction(m: int, on: bool) -> None:
+    """Speculative expert prediction on or off for later launches (MoE models; off by default)."""
     _check(load().mkd_set_expert_prediction(m, 1 if on else 0))
 
 
